@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark of the R-SWA decode hot path on one MI355X.
+
+A step is one fused append + attend decode step of the 40-page workload
+(B = 32 sequences, H = 16 heads, d = 128, L_m = 10272, n = 128, bf16, one
+attention layer): one call of rswa_decode_attn. W warm-up steps run first
+(they also fill the 128-slot window), then exactly K steps are timed with HIP
+events on the launch stream. All inputs (reference K/V, per-step q/k/v) are
+resident in HBM before the timed region.
+
+Printed: one JSON line. `value` is decode tokens/s (B / step time). The
+`roofline` object prices the decode kernel's algorithmic bytes (every visible
+K/V row once, plus q, out and the new k/v) against the 8 TB/s HBM peak.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same step.
+Secondary lines of the same JSON: the full-attention contrast (cache L_m + T)
+at a few decode lengths, and the packed 32K masked forward on matrix cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "R-SWA decode-attn tokens/s and HBM GB/s (%peak) at L_m=10272, n=128, B=32"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+COUNTERS = os.path.join(ROOT, "profiles", "decode_40page_counters.txt")
+DECODE_SRC = os.path.join(ROOT, "reference_sliding_window_amd", "csrc", "rswa_decode.hip")
+
+
+def decode_bytes(B, H, d, L, n, T, elt=2):
+    """Algorithmic bytes of one decode step: visible K and V rows once, plus q, out, k_new, v_new."""
+    return B * H * (L + min(n, T)) * d * elt * 2 + 4 * B * H * d * elt
+
+
+def masked_flops(N, L_m, n, H, d, prefix_full=False):
+    """4 d FLOP per visible (query, key) pair of the two-segment mask."""
+    pre = L_m * L_m if prefix_full else L_m * (L_m + 1) // 2
+    outs = N - L_m
+    win = sum(min(n, t) for t in range(1, outs + 1)) if outs > 0 else 0
+    return 4 * d * H * (pre + L_m * max(outs, 0) + win)
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(per_launch_units):
+    """HBM traffic of the decode kernel from the committed rocprofv3 counter summary,
+    or None if the summary is missing or was taken on different kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None
+    kv = {}
+    for ln in open(COUNTERS):
+        if ":" in ln and not ln.startswith("#"):
+            k, v = ln.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != source_sha(DECODE_SRC):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def event_time_ms(fn, iters, stream):
+    import torch
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(iters):
+        fn(i)
+    b.record(stream)
+    b.synchronize()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
+def cpu_baseline(w, kref, vref, T, budget_s):
+    """Time the oracle on (sequence, head) pairs of decode step T until budget_s elapses."""
+    import oracle.rswa as orc
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    first = max(1, T - w.window + 1)
+    q, k, v = wl.steps_qkv(w, first, T)
+    pairs = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(len(pairs))
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        done, t0 = 0, time.perf_counter()
+        while done < len(order) and time.perf_counter() - t0 < budget_s:
+            b, h = pairs[order[done]]
+            orc.decode_output(wl.to_f64(q[-1, b, h], w.dtype), wl.to_f64(kref[b, h], w.dtype),
+                              wl.to_f64(vref[b, h], w.dtype), wl.to_f64(k[:, b, h], w.dtype),
+                              wl.to_f64(v[:, b, h], w.dtype), first, w.ref_len, w.window, T, w.scale)
+            done += 1
+        el = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    step_s = el / done * len(pairs)
+    return {"value": w.batch / step_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"40-page decode step T={T}: {done} of {len(pairs)} (sequence, head) pairs "
+                      f"in {el:.1f} s on 1 thread (BLAS limited to 1), scaled to all {len(pairs)}; "
+                      f"host has {len(os.sched_getaffinity(0))} cores available"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2048)
+    ap.add_argument("--warmup", type=int, default=256)
+    ap.add_argument("--splits", type=int, default=0, help="decode key splits per (seq, head); 0 = library")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the contrast and masked lines")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (requested --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "R-SWA decode shards by sequence and head with no exchange, so the per-GPU figure "
+              "is the N=1 line.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import reference_sliding_window_amd as rs
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    rs.library()  # fail loudly if the HIP library is missing
+
+    w = wl.FORTY_PAGE
+    B, H, d, L, n = w.batch, w.heads, w.head_dim, w.ref_len, w.window
+    K, W = args.steps, args.warmup
+    t_setup = time.perf_counter()
+    kref, vref = wl.ref_kv_all(w)
+    cache = rs.KVCache.allocate([L] * B, H, d, n, dtype=rs.RSWA_BF16)
+    ref_base = torch.arange(B, dtype=torch.int64, device="cuda") * (H * L * d)
+    kd = torch.from_numpy(kref.reshape(-1).view(np.int16)).view(torch.bfloat16).cuda()
+    vd = torch.from_numpy(vref.reshape(-1).view(np.int16)).view(torch.bfloat16).cuda()
+    rs.rswa_cache_init(cache.desc, kd, vd, ref_base)
+    torch.cuda.synchronize()
+    del kd, vd
+    steps_total = W + K
+    qs = torch.empty((steps_total, B, H, d), dtype=torch.bfloat16, device="cuda")
+    ks = torch.empty_like(qs)
+    vs = torch.empty_like(qs)
+    for c0 in range(0, steps_total, 512):
+        c1 = min(steps_total, c0 + 512)
+        q, k, v = wl.steps_qkv(w, c0 + 1, c1)
+        for dst, src in ((qs, q), (ks, k), (vs, v)):
+            dst[c0:c1].copy_(torch.from_numpy(src.view(np.int16)).view(torch.bfloat16))
+    ws = cache.workspace(args.splits)
+    out = torch.empty((B, H, d), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    setup_s = time.perf_counter() - t_setup
+
+    def step(i):
+        rs.rswa_decode_attn(cache.desc, qs[i], out, ks[i], vs[i], 0.0, args.splits, ws, stream=stream)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    ms = event_time_ms(lambda i: step(W + i), K, stream)
+    ms_per_step = ms / K
+    flags = rs.rswa_check_device_error(cache.desc)
+    if flags:
+        print(f"device error flags {flags}", file=sys.stderr)
+        sys.exit(1)
+    alg_bytes = sum(decode_bytes(B, H, d, L, n, T) for T in range(W + 1, W + K + 1)) / K
+    achieved = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    traffic = read_traffic(1)
+    result = {
+        "metric": METRIC,
+        "value": B / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "heads": H, "head_dim": d, "ref_len": L,
+                   "window": n, "layers": 1, "timed_decode_steps": f"T={W + 1}..{W + K}",
+                   "splits": args.splits or "library"},
+        "hbm_GBps": achieved,
+        "hbm_frac_of_peak": achieved / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "rswa decode step (split-K attention + split merge), one call",
+                     "algorithmic_bytes_per_launch": alg_bytes},
+    }
+    del qs, ks, vs
+
+    if not args.no_secondary:
+        # full-attention contrast: the same kernels with a window >= every output (cache L_m + T)
+        Tmax = w.steps
+        con = rs.KVCache.allocate([L] * B, H, d, Tmax, dtype=rs.RSWA_BF16)
+        con.k.normal_(0.0, w.sigma_kv)
+        con.v.normal_(0.0, w.sigma_kv)
+        cws = con.workspace()
+        q1 = torch.randn((B, H, d), device="cuda").to(torch.bfloat16)
+        contrast = {}
+        for T in (256, 2048, 4096, 6144):
+            con.step.fill_(T)   # attend-only call over the L_m + T cached slots
+            ms_c = event_time_ms(lambda i: rs.rswa_decode_attn(con.desc, q1, out, None, None, 0.0, 0, cws,
+                                                             stream=stream), 20, stream) / 20
+            contrast[str(T)] = {"ms_per_step": ms_c, "cache_slots": L + T,
+                                "GBps": decode_bytes(B, H, d, L, Tmax, T) / (ms_c * 1e-3) / 1e9}
+        # the R-SWA cache at the same attend-only call, for a like-for-like comparison
+        ms_r = event_time_ms(lambda i: rs.rswa_decode_attn(cache.desc, q1, out, None, None, 0.0, 0, ws,
+                                                         stream=stream), 20, stream) / 20
+        result["contrast_full_attention"] = {
+            "what": "attend-only decode call; full attention keeps L_m + T slots (window >= all outputs), "
+                    "R-SWA keeps L_m + 128",
+            "full_attention_per_T": contrast,
+            "rswa_attend_only_ms": ms_r,
+            "rswa_fused_step_ms": ms_per_step}
+        del con
+        # packed 32K masked forward (matrix cores)
+        mw = wl.PACKED_32K
+        Q, Kp, Vp = wl.packed_qkv(mw)
+        to_d = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        Qd, Kd, Vd = to_d(Q), to_d(Kp), to_d(Vp)
+        Od = torch.empty_like(Qd)
+        masked = {}
+        for mode, name in ((rs.RSWA_PREFIX_CAUSAL, "prefix_causal"), (rs.RSWA_PREFIX_FULL, "prefix_full")):
+            run = lambda i: rs.rswa_masked_attn(Qd, Kd, Vd, Od, mw.seq_len, mw.ref_len, mw.window, mw.heads,
+                                                mw.head_dim, rs.RSWA_BF16, mode, 0.0, stream=stream)
+            run(0)
+            run(0)
+            ms_m = event_time_ms(run, 10, stream) / 10
+            fl = masked_flops(mw.seq_len, mw.ref_len, mw.window, mw.heads, mw.head_dim,
+                              mode == rs.RSWA_PREFIX_FULL)
+            masked[name] = {"ms": ms_m, "algorithmic_flop": fl, "TFLOPs": fl / (ms_m * 1e-3) / 1e12,
+                            "frac_of_bf16_peak": fl / (ms_m * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+        result["masked_32k"] = {"workload": mw.name, "seq_len": mw.seq_len, "ref_len": mw.ref_len,
+                                "window": mw.window, "heads": mw.heads, **masked}
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, kref, vref, W + K, args.cpu_seconds)
+    result["setup_s"] = setup_s
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+/*
+ * rswa.h -- C ABI of librswa: Reference Sliding Window Attention (R-SWA) on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * R-SWA, as the pages define it: every query attends to the whole reference
+ * segment P = {1..L_m} (vision tokens + prompt, encoded once and never
+ * updated) plus the causal window D_n(t) of the n most recent output tokens
+ *   WeThinkIn "Unlimited OCR Works：一篇读懂 R-SWA 如何把长文档 OCR 从 for-loop
+ *   推向 one-shot", section 方法展开.3, Eqs. (1)-(4);
+ * so the KV cache holds L_m + min(n, T) entries after T outputs (same page,
+ * section 方法展开.4, Eq. (6)). The cache is a queue of capacity m + n whose
+ * oldest output (position m+1) is evicted by each new token
+ *   夜雨聆风 "多模态文档解析开源新进展:Unlimited OCR技术方案", section
+ *   "为什么它能”无限”读下去？关键在 KV cache 恒定";
+ * i.e. a fixed-capacity output KV buffer of width n on top of the reference
+ * KV cache (yhxrc.cn news article, section "R-SWA 如何穩住長程解碼？").
+ *
+ * General rules for every call
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates no memory and keeps no mutable global state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls
+ *    only enqueue work on it and return; none synchronises except
+ *    rswa_check_device_error.
+ *  - Arguments are validated on the host before anything is enqueued. On an
+ *    error the call returns a negative rswa_status_t and enqueues nothing.
+ *    Errors from the HIP runtime at launch map to RSWA_ERR_HIP.
+ *  - Facts only visible on the device (per-sequence lengths and counters) are
+ *    checked by the kernels; a violation sets a bit in the cache's device
+ *    error word (RSWA_DEVERR_*), skips the affected sequence and is read back
+ *    by rswa_check_device_error.
+ *  - Tensors of element type rswa_dtype_t; bf16 means IEEE bfloat16 bit
+ *    patterns. All pointers must be 16-byte aligned.
+ *  - Nothing is thrown across the ABI and nothing aborts.
+ */
+#ifndef RSWA_H
+#define RSWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RSWA_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define RSWA_API __attribute__((visibility("default")))
+#else
+#define RSWA_API
+#endif
+
+typedef enum {
+  RSWA_OK = 0,
+  RSWA_ERR_NULL = -1,        /* a required pointer is NULL                          */
+  RSWA_ERR_SHAPE = -2,       /* a size/shape argument is out of range               */
+  RSWA_ERR_UNSUPPORTED = -3, /* valid but not implemented (dtype, head_dim, mode)   */
+  RSWA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                    */
+  RSWA_ERR_CAPACITY = -5,    /* sizes would overflow 32-bit slot or 64-bit offsets  */
+  RSWA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required          */
+  RSWA_ERR_STATE = -7,       /* device-side state was found invalid                 */
+  RSWA_ERR_HIP = -8          /* the HIP runtime reported an error                   */
+} rswa_status_t;
+
+typedef enum { RSWA_BF16 = 0, RSWA_FP32 = 1 } rswa_dtype_t;
+
+/* Visibility of rows inside the reference prefix in the packed form. The pages
+ * define N(t) for output tokens only; prefix rows are causal by default. */
+typedef enum { RSWA_PREFIX_CAUSAL = 0, RSWA_PREFIX_FULL = 1 } rswa_prefix_mode_t;
+
+/* Bits of the device error word. */
+#define RSWA_DEVERR_REF_LEN 1   /* ref_len[b] < 0 or > max_ref_len                   */
+#define RSWA_DEVERR_STEP 2      /* step[b] < 0, or step[b] would overflow int32      */
+#define RSWA_DEVERR_EMPTY 4     /* decode with nothing visible (L_m = 0 and T = 0)   */
+#define RSWA_DEVERR_ALIGN 8     /* seq_base[b] / ref_base[b] not 16-byte aligned     */
+
+/*
+ * KV cache descriptor (plain struct, caller-owned, passed by pointer).
+ *
+ * Sequence b owns one contiguous block in each of the pools k and v, starting
+ * at ELEMENT offset seq_base[b], laid out [H][ref_len[b] + window][head_dim]:
+ *   head h, slot s  ->  pool + seq_base[b] + ((int64)h*(ref_len[b]+window) + s)*head_dim
+ * Slots 0 .. ref_len[b]-1 hold the reference segment (position p in slot p-1).
+ * Output token T (T = 1, 2, ...) is written to slot
+ *   ref_len[b] + ((T - 1) mod window)
+ * which overwrites output T - window, the oldest one, exactly when the queue
+ * of capacity L_m + n is full. This slot rule is part of the ABI: a caller may
+ * build a cache state directly. After T outputs, slots [0, L_m + min(n, T))
+ * are occupied and all of them are visible to the next query (attention does
+ * not depend on key order).
+ *
+ * step[b] is T, the number of outputs appended so far. It lives on the device
+ * so that decode steps need no host synchronisation.
+ */
+typedef struct rswa_cache {
+  int32_t batch;        /* B >= 1                                                 */
+  int32_t num_heads;    /* H >= 1; MHA: query heads == KV heads                   */
+  int32_t head_dim;     /* d in {64, 128}                                         */
+  int32_t window;       /* n >= 1 (the pages' default is 128)                     */
+  int32_t max_ref_len;  /* host-side bound: 0 <= ref_len[b] <= max_ref_len        */
+  int32_t dtype;        /* rswa_dtype_t of the pools and of q/out/k_new/v_new     */
+  void *k;              /* device pool of keys                                    */
+  void *v;              /* device pool of values                                  */
+  const int64_t *seq_base; /* device [B], element offsets (multiple of 16 bytes)  */
+  const int32_t *ref_len;  /* device [B], L_m per sequence                        */
+  int32_t *step;           /* device [B], T per sequence                          */
+  int32_t *error;          /* device, one int32 word of RSWA_DEVERR_* bits        */
+} rswa_cache_t;
+
+/* Library ABI version (RSWA_ABI_VERSION). */
+RSWA_API int32_t rswa_abi_version(void);
+
+/* Static string for a status code; never NULL. */
+RSWA_API const char *rswa_status_str(int32_t status);
+
+/*
+ * Write the reference segment into the cache ("encoded once, never updated":
+ * 夜雨聆风 page, same section as above) and reset step[b] = 0 for every b.
+ * k_ref, v_ref: device; sequence b's reference at element offset ref_base[b]
+ * (device [B]), laid out [H][ref_len[b]][head_dim], same dtype as the cache.
+ * When max_ref_len == 0 the three may be NULL. Does not touch the window slots.
+ */
+RSWA_API rswa_status_t rswa_cache_init(const rswa_cache_t *cache, const void *k_ref, const void *v_ref,
+                              const int64_t *ref_base, void *stream);
+
+/*
+ * Append one output token per sequence (and evict the oldest output once the
+ * window is full): for each b with active == NULL or active[b] != 0, write
+ * k_new[b][h][:], v_new[b][h][:] into slot ref_len[b] + (step[b] mod window)
+ * of every head h, then step[b] += 1. Bit-exact copy.
+ * k_new, v_new: device [B][H][head_dim]; active: NULL or device uint8 [B].
+ */
+RSWA_API rswa_status_t rswa_append_kv(const rswa_cache_t *cache, const void *k_new, const void *v_new,
+                             const uint8_t *active, void *stream);
+
+/*
+ * Workspace bytes needed by rswa_decode_attn for this cache descriptor and
+ * split count (0 = the library's choice). Returns 0 for an invalid
+ * descriptor. The workspace holds per-split partial softmax states.
+ */
+RSWA_API size_t rswa_decode_workspace_size(const rswa_cache_t *cache, int32_t num_splits);
+
+/*
+ * One decode step of attention for every sequence (WeThinkIn page, Eqs.
+ * (1)-(4)): out[b][h] = softmax(scale * K_vis q[b][h]) V_vis over the visible
+ * slots [0, L_m + min(n, T)) of sequence b, head h.
+ *
+ *  q, out       device [B][H][head_dim], cache dtype. bf16 output is rounded
+ *               to nearest even from the fp32 result.
+ *  k_new, v_new both NULL: attend over the cache as it is (T = step[b]).
+ *               both non-NULL (device [B][H][head_dim]): fused append+attend.
+ *               The new token is appended exactly as rswa_append_kv would do,
+ *               then attended to (T = step[b] + 1), and step[b] is incremented.
+ *               The evicted entry is never read.
+ *  scale        softmax scale; 0 selects 1/sqrt(head_dim). Must be finite.
+ *  num_splits   0 = the library's choice; otherwise the number of key chunks
+ *               per (sequence, head) merged at the end (>= 1). The result does
+ *               not depend on it beyond fp32 rounding.
+ *  workspace    device, >= rswa_decode_workspace_size(cache, num_splits) bytes.
+ *
+ * Accumulation is fp32. Softmax runs in base 2 with log2(e) folded into the
+ * scale.
+ */
+RSWA_API rswa_status_t rswa_decode_attn(const rswa_cache_t *cache, const void *q, void *out,
+                               const void *k_new, const void *v_new, float scale,
+                               int32_t num_splits, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/*
+ * Packed (teacher-forced) R-SWA forward over one sequence of seq_len tokens:
+ * row i attends to key j iff j <= i and (j < ref_len or i - j < window); with
+ * RSWA_PREFIX_FULL, rows i < ref_len instead attend to all j < ref_len. For a
+ * row i >= ref_len this is N(t) of the WeThinkIn page's Eqs. (1)-(2) for the
+ * query formed at position i. q, k, v, out: device [seq_len][num_heads][head_dim]
+ * bf16 (row-major, heads interleaved). Only RSWA_BF16 and head_dim 128 are
+ * implemented. QK^T and PV run on bf16 matrix cores with fp32 accumulation;
+ * the probabilities are rounded to bf16 before the PV product.
+ */
+RSWA_API rswa_status_t rswa_masked_attn(const void *q, const void *k, const void *v, void *out,
+                               int32_t seq_len, int32_t ref_len, int32_t window,
+                               int32_t num_heads, int32_t head_dim, int32_t dtype,
+                               int32_t prefix_mode, float scale, void *stream);
+
+/*
+ * Synchronise `stream`, read the cache's device error word into *flags
+ * (RSWA_DEVERR_* bits, 0 = none) and clear it. Returns RSWA_ERR_STATE when a
+ * bit was set, RSWA_OK otherwise.
+ */
+RSWA_API rswa_status_t rswa_check_device_error(const rswa_cache_t *cache, int32_t *flags, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RSWA_H */

@@ -1,0 +1,256 @@
+// Host side of librswa: argument validation (before anything is enqueued),
+// the decode split plan and workspace layout, and the extern "C" entry points
+// declared in include/rswa.h.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <algorithm>
+
+#include "rswa_internal.h"
+
+namespace rswa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Host-visible checks of a cache descriptor (device arrays are checked by the kernels).
+rswa_status_t check_cache(const rswa_cache_t *c) {
+  if (c == nullptr) return RSWA_ERR_NULL;
+  if (c->k == nullptr || c->v == nullptr || c->seq_base == nullptr || c->ref_len == nullptr ||
+      c->step == nullptr || c->error == nullptr)
+    return RSWA_ERR_NULL;
+  if (c->dtype != RSWA_BF16 && c->dtype != RSWA_FP32) return RSWA_ERR_UNSUPPORTED;
+  if (c->batch < 1 || c->num_heads < 1 || c->window < 1 || c->max_ref_len < 0)
+    return RSWA_ERR_SHAPE;
+  if (c->head_dim != 64 && c->head_dim != 128) return RSWA_ERR_UNSUPPORTED;
+  // slot indices are int32; one sequence block must be addressable in int64
+  const int64_t max_len = (int64_t)c->max_ref_len + c->window;
+  if (max_len > INT32_MAX) return RSWA_ERR_CAPACITY;
+  if ((int64_t)c->batch * c->num_heads > INT32_MAX / 2) return RSWA_ERR_CAPACITY;
+  if (!aligned16(c->k) || !aligned16(c->v) || !aligned16(c->error)) return RSWA_ERR_ALIGN;
+  return RSWA_OK;
+}
+
+bool verbose() {
+  const char *e = getenv("RSWA_LOG");
+  return e != nullptr && e[0] == '1';
+}
+
+}  // namespace
+
+SplitPlan plan_decode_splits(int32_t batch, int32_t heads, int32_t max_len, int32_t requested) {
+  // Default: enough workgroups to give every one of the 256 CUs several
+  // resident workgroups (>= 2048 in total), but never chunks below 64 slots.
+  constexpr int64_t kTargetWorkgroups = 2048;
+  constexpr int32_t kMinChunk = 64;
+  const int64_t bh = (int64_t)batch * heads;
+  const int32_t len = max_len > 0 ? max_len : 1;
+  int64_t s = requested > 0 ? requested : (kTargetWorkgroups + bh - 1) / bh;
+  if (requested <= 0) s = std::min<int64_t>(s, (len + kMinChunk - 1) / kMinChunk);
+  s = std::max<int64_t>(1, std::min<int64_t>(s, len));
+  int64_t chunk = (len + s - 1) / s;
+  if (requested <= 0) chunk = round_up((size_t)chunk, kMinChunk);
+  const int64_t splits = (len + chunk - 1) / chunk;
+  return SplitPlan{(int32_t)splits, (int32_t)chunk};
+}
+
+WorkspaceLayout decode_workspace_layout(int32_t batch, int32_t heads, int32_t head_dim,
+                                        int32_t splits) {
+  WorkspaceLayout w{};
+  const size_t units = (size_t)batch * heads * splits;
+  w.part_o = 0;
+  w.part_ml = round_up(units * head_dim * sizeof(float), 256);
+  w.seq_state = w.part_ml + round_up(units * 2 * sizeof(float), 256);
+  w.total = w.seq_state + round_up((size_t)batch * sizeof(int32_t), 256);
+  return w;
+}
+
+}  // namespace rswa
+
+using namespace rswa;
+
+extern "C" {
+
+int32_t rswa_abi_version(void) { return RSWA_ABI_VERSION; }
+
+const char *rswa_status_str(int32_t status) {
+  switch (status) {
+    case RSWA_OK: return "ok";
+    case RSWA_ERR_NULL: return "required pointer is NULL";
+    case RSWA_ERR_SHAPE: return "size or shape argument out of range";
+    case RSWA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim or mode";
+    case RSWA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case RSWA_ERR_CAPACITY: return "sizes overflow the index range";
+    case RSWA_ERR_WORKSPACE: return "workspace missing or too small";
+    case RSWA_ERR_STATE: return "device-side state invalid";
+    case RSWA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+rswa_status_t rswa_cache_init(const rswa_cache_t *cache, const void *k_ref, const void *v_ref,
+                              const int64_t *ref_base, void *stream) {
+  rswa_status_t st = check_cache(cache);
+  if (st != RSWA_OK) return st;
+  // An empty reference (max_ref_len == 0) needs no source buffers.
+  if (cache->max_ref_len > 0 && (k_ref == nullptr || v_ref == nullptr || ref_base == nullptr))
+    return RSWA_ERR_NULL;
+  if (!aligned16(k_ref) || !aligned16(v_ref)) return RSWA_ERR_ALIGN;
+  InitParams p{};
+  p.k_ref = k_ref;
+  p.v_ref = v_ref;
+  p.ref_base = ref_base;
+  p.k = cache->k;
+  p.v = cache->v;
+  p.seq_base = cache->seq_base;
+  p.ref_len = cache->ref_len;
+  p.step = cache->step;
+  p.error = cache->error;
+  p.batch = cache->batch;
+  p.heads = cache->num_heads;
+  p.window = cache->window;
+  p.max_ref_len = cache->max_ref_len;
+  const hipError_t e = launch_cache_init(p, cache->dtype, cache->head_dim,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
+}
+
+rswa_status_t rswa_append_kv(const rswa_cache_t *cache, const void *k_new, const void *v_new,
+                             const uint8_t *active, void *stream) {
+  rswa_status_t st = check_cache(cache);
+  if (st != RSWA_OK) return st;
+  if (k_new == nullptr || v_new == nullptr) return RSWA_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return RSWA_ERR_ALIGN;
+  AppendParams p{};
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.active = active;
+  p.k = cache->k;
+  p.v = cache->v;
+  p.seq_base = cache->seq_base;
+  p.ref_len = cache->ref_len;
+  p.step = cache->step;
+  p.error = cache->error;
+  p.batch = cache->batch;
+  p.heads = cache->num_heads;
+  p.window = cache->window;
+  p.max_ref_len = cache->max_ref_len;
+  const hipError_t e = launch_append(p, cache->dtype, cache->head_dim,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
+}
+
+size_t rswa_decode_workspace_size(const rswa_cache_t *cache, int32_t num_splits) {
+  if (check_cache(cache) != RSWA_OK || num_splits < 0) return 0;
+  const SplitPlan plan = plan_decode_splits(cache->batch, cache->num_heads,
+                                            cache->max_ref_len + cache->window, num_splits);
+  return decode_workspace_layout(cache->batch, cache->num_heads, cache->head_dim, plan.splits)
+      .total;
+}
+
+rswa_status_t rswa_decode_attn(const rswa_cache_t *cache, const void *q, void *out,
+                               const void *k_new, const void *v_new, float scale,
+                               int32_t num_splits, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  rswa_status_t st = check_cache(cache);
+  if (st != RSWA_OK) return st;
+  if (q == nullptr || out == nullptr) return RSWA_ERR_NULL;
+  if ((k_new == nullptr) != (v_new == nullptr)) return RSWA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out)) return RSWA_ERR_ALIGN;
+  if (k_new != nullptr && (!aligned16(k_new) || !aligned16(v_new))) return RSWA_ERR_ALIGN;
+  if (!isfinite(scale)) return RSWA_ERR_SHAPE;
+  if (num_splits < 0) return RSWA_ERR_SHAPE;
+  const SplitPlan plan = plan_decode_splits(cache->batch, cache->num_heads,
+                                            cache->max_ref_len + cache->window, num_splits);
+  const WorkspaceLayout ws = decode_workspace_layout(cache->batch, cache->num_heads,
+                                                     cache->head_dim, plan.splits);
+  if (workspace == nullptr) return RSWA_ERR_WORKSPACE;
+  if (workspace_bytes < ws.total) return RSWA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return RSWA_ERR_ALIGN;
+  char *wsb = static_cast<char *>(workspace);
+  DecodeParams p{};
+  p.q = q;
+  p.out = out;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k = cache->k;
+  p.v = cache->v;
+  p.seq_base = cache->seq_base;
+  p.ref_len = cache->ref_len;
+  p.step = cache->step;
+  p.error = cache->error;
+  p.part_o = reinterpret_cast<float *>(wsb + ws.part_o);
+  p.part_ml = reinterpret_cast<float *>(wsb + ws.part_ml);
+  p.seq_state = reinterpret_cast<int32_t *>(wsb + ws.seq_state);
+  p.batch = cache->batch;
+  p.heads = cache->num_heads;
+  p.window = cache->window;
+  p.max_ref_len = cache->max_ref_len;
+  p.splits = plan.splits;
+  p.chunk = plan.chunk;
+  const float sc = scale == 0.f ? 1.f / sqrtf((float)cache->head_dim) : scale;
+  p.scale_log2 = sc * kLog2e;
+  if (verbose()) {
+    fprintf(stderr, "[rswa] decode B=%d H=%d d=%d n=%d maxL=%d splits=%d chunk=%d fused=%d\n",
+            p.batch, p.heads, cache->head_dim, p.window, p.max_ref_len, p.splits, p.chunk,
+            k_new != nullptr);
+  }
+  const hipError_t e = launch_decode(p, cache->dtype, cache->head_dim,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
+}
+
+rswa_status_t rswa_masked_attn(const void *q, const void *k, const void *v, void *out,
+                               int32_t seq_len, int32_t ref_len, int32_t window,
+                               int32_t num_heads, int32_t head_dim, int32_t dtype,
+                               int32_t prefix_mode, float scale, void *stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return RSWA_ERR_NULL;
+  if (seq_len < 0 || ref_len < 0 || ref_len > seq_len || window < 1 || num_heads < 1)
+    return RSWA_ERR_SHAPE;
+  if (dtype != RSWA_BF16 || head_dim != 128) return RSWA_ERR_UNSUPPORTED;
+  if (prefix_mode != RSWA_PREFIX_CAUSAL && prefix_mode != RSWA_PREFIX_FULL)
+    return RSWA_ERR_UNSUPPORTED;
+  if ((int64_t)seq_len * num_heads * head_dim > ((int64_t)1 << 40)) return RSWA_ERR_CAPACITY;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RSWA_ERR_ALIGN;
+  if (!isfinite(scale)) return RSWA_ERR_SHAPE;
+  if (seq_len == 0) return RSWA_OK;
+  MaskedParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.seq_len = seq_len;
+  p.ref_len = ref_len;
+  p.window = window;
+  p.heads = num_heads;
+  p.prefix_mode = prefix_mode;
+  const float sc = scale == 0.f ? 1.f / sqrtf((float)head_dim) : scale;
+  p.scale_log2 = sc * kLog2e;
+  const hipError_t e = launch_masked(p, head_dim, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
+}
+
+rswa_status_t rswa_check_device_error(const rswa_cache_t *cache, int32_t *flags, void *stream) {
+  if (cache == nullptr || cache->error == nullptr || flags == nullptr) return RSWA_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t word = 0;
+  if (hipMemcpyAsync(&word, cache->error, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return RSWA_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return RSWA_ERR_HIP;
+  *flags = word;
+  if (word != 0) {
+    if (launch_clear_word(cache->error, s) != hipSuccess) return RSWA_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return RSWA_ERR_HIP;
+    return RSWA_ERR_STATE;
+  }
+  return RSWA_OK;
+}
+
+}  // extern "C"

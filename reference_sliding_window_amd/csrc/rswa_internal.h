@@ -1,0 +1,93 @@
+// Internal declarations shared by the host API and the kernel files of librswa.
+// Not part of the ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/rswa.h"
+
+namespace rswa {
+
+// Work split of one decode launch: every (sequence, head) is cut into `splits`
+// chunks of `chunk` key slots; each chunk is one workgroup.
+struct SplitPlan {
+  int32_t splits;
+  int32_t chunk;
+};
+
+// Chooses the split plan from host-known sizes only (the per-sequence lengths
+// live on the device). requested = 0 selects the library's choice.
+SplitPlan plan_decode_splits(int32_t batch, int32_t heads, int32_t max_len, int32_t requested);
+
+// Byte layout of the decode workspace.
+struct WorkspaceLayout {
+  size_t part_o;     // float [B*H][splits][d]: unnormalised partial outputs
+  size_t part_ml;    // float [B*H][splits][2]: running max (base 2) and sum
+  size_t seq_state;  // int32 [B]: new step value for the merge pass, or -1
+  size_t total;
+};
+WorkspaceLayout decode_workspace_layout(int32_t batch, int32_t heads, int32_t head_dim,
+                                        int32_t splits);
+
+struct DecodeParams {
+  const void *q;
+  void *out;
+  const void *k_new;  // nullptr: attend only
+  const void *v_new;
+  void *k;
+  void *v;
+  const int64_t *seq_base;
+  const int32_t *ref_len;
+  int32_t *step;
+  int32_t *error;
+  float *part_o;
+  float *part_ml;
+  int32_t *seq_state;
+  int32_t batch, heads, window, max_ref_len;
+  int32_t splits, chunk;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+struct AppendParams {
+  const void *k_new;
+  const void *v_new;
+  const uint8_t *active;
+  void *k;
+  void *v;
+  const int64_t *seq_base;
+  const int32_t *ref_len;
+  int32_t *step;
+  int32_t *error;
+  int32_t batch, heads, window, max_ref_len;
+};
+
+struct InitParams {
+  const void *k_ref;
+  const void *v_ref;
+  const int64_t *ref_base;
+  void *k;
+  void *v;
+  const int64_t *seq_base;
+  const int32_t *ref_len;
+  int32_t *step;
+  int32_t *error;
+  int32_t batch, heads, window, max_ref_len;
+};
+
+struct MaskedParams {
+  const void *q;
+  const void *k;
+  const void *v;
+  void *out;
+  int32_t seq_len, ref_len, window, heads, prefix_mode;
+  float scale_log2;
+};
+
+// Launchers (enqueue only; return the launch's hipError_t).
+hipError_t launch_cache_init(const InitParams &p, int32_t dtype, int32_t head_dim, hipStream_t s);
+hipError_t launch_append(const AppendParams &p, int32_t dtype, int32_t head_dim, hipStream_t s);
+hipError_t launch_decode(const DecodeParams &p, int32_t dtype, int32_t head_dim, hipStream_t s);
+hipError_t launch_masked(const MaskedParams &p, int32_t head_dim, hipStream_t s);
+hipError_t launch_clear_word(int32_t *word, hipStream_t s);
+
+}  // namespace rswa

@@ -1,0 +1,139 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+the header declares, and rejects bad arguments on the host with the
+documented status before anything is enqueued (no HIP call is reached)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import reference_sliding_window_amd as rs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rswa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(rs.LIB_PATH), reason="librswa.so not built")
+
+A = 0x7f0000000000  # a fake, 16-byte aligned device address; never dereferenced here
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"RSWA_API\s+[\w\s\*]*?\b(rswa_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls_and_helpers():
+    names = header_functions()
+    for n in ("rswa_cache_init", "rswa_append_kv", "rswa_decode_attn", "rswa_masked_attn"):
+        assert n in names
+    assert set(names) == set(rs.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = rs.library()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", rs.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (rswa_\w+)", out))
+    assert set(header_functions()) <= exported
+
+
+def test_abi_version_and_status_strings():
+    ver = int(re.search(r"#define RSWA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert rs.rswa_abi_version() == ver
+    for code in range(0, -9, -1):
+        assert rs.rswa_status_str(code) not in ("", "unknown status")
+    assert rs.rswa_status_str(-99) == "unknown status"
+
+
+def good_desc(**kw):
+    d = dict(batch=2, num_heads=4, head_dim=128, window=8, max_ref_len=100, dtype=rs.RSWA_BF16,
+             k=A, v=A + 0x100000, seq_base=A + 0x200000, ref_len=A + 0x300000, step=A + 0x400000,
+             error=A + 0x500000)
+    d.update(kw)
+    return rs.CacheDesc(**d)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 96, rs.RSWA_ERR_UNSUPPORTED),
+    ("head_dim", 0, rs.RSWA_ERR_UNSUPPORTED),
+    ("dtype", 7, rs.RSWA_ERR_UNSUPPORTED),
+    ("batch", 0, rs.RSWA_ERR_SHAPE),
+    ("num_heads", -1, rs.RSWA_ERR_SHAPE),
+    ("window", 0, rs.RSWA_ERR_SHAPE),
+    ("max_ref_len", -5, rs.RSWA_ERR_SHAPE),
+    ("max_ref_len", 2 ** 31 - 4, rs.RSWA_ERR_CAPACITY),
+    ("k", None, rs.RSWA_ERR_NULL),
+    ("step", None, rs.RSWA_ERR_NULL),
+    ("error", None, rs.RSWA_ERR_NULL),
+    ("v", A + 8, rs.RSWA_ERR_ALIGN),
+])
+def test_bad_descriptor_rejected_by_every_cache_call(field, value, status):
+    desc = good_desc(**{field: value})
+    assert rs.rswa_append_kv(desc, A, A, check=False) == status
+    assert rs.rswa_cache_init(desc, A, A, A, check=False) == status
+    assert rs.rswa_decode_attn(desc, A, A, workspace=A, workspace_bytes=1 << 30, check=False) == status
+    assert rs.rswa_decode_workspace_size(desc, 0) == 0
+
+
+def test_decode_argument_checks():
+    desc = good_desc()
+    ws = rs.rswa_decode_workspace_size(desc, 0)
+    assert ws > 0
+    call = lambda **kw: rs.rswa_decode_attn(desc, **{**dict(q=A, out=A, workspace=A, workspace_bytes=ws), **kw},
+                                             check=False)
+    assert call(q=None) == rs.RSWA_ERR_NULL
+    assert call(out=None) == rs.RSWA_ERR_NULL
+    assert call(k_new=A) == rs.RSWA_ERR_NULL          # k_new without v_new
+    assert call(v_new=A) == rs.RSWA_ERR_NULL
+    assert call(q=A + 4) == rs.RSWA_ERR_ALIGN
+    assert call(k_new=A + 2, v_new=A) == rs.RSWA_ERR_ALIGN
+    assert call(scale=math.nan) == rs.RSWA_ERR_SHAPE
+    assert call(scale=math.inf) == rs.RSWA_ERR_SHAPE
+    assert call(num_splits=-1) == rs.RSWA_ERR_SHAPE
+    assert call(workspace=None, workspace_bytes=0) == rs.RSWA_ERR_WORKSPACE
+    assert call(workspace_bytes=ws - 1) == rs.RSWA_ERR_WORKSPACE
+    assert call(workspace=A + 4) == rs.RSWA_ERR_ALIGN
+
+
+def test_workspace_grows_with_splits():
+    desc = good_desc(max_ref_len=10272, window=128, batch=32, num_heads=16)
+    s1 = rs.rswa_decode_workspace_size(desc, 1)
+    s16 = rs.rswa_decode_workspace_size(desc, 16)
+    assert 0 < s1 < s16
+    # 16 splits: 32*16*16 partial states of 128 floats plus (max, sum) pairs
+    assert s16 >= 32 * 16 * 16 * (128 + 2) * 4
+
+
+def test_append_and_init_argument_checks():
+    desc = good_desc()
+    assert rs.rswa_append_kv(desc, None, A, check=False) == rs.RSWA_ERR_NULL
+    assert rs.rswa_append_kv(desc, A, A + 8, check=False) == rs.RSWA_ERR_ALIGN
+    assert rs.rswa_cache_init(desc, A, A, None, check=False) == rs.RSWA_ERR_NULL
+    assert rs.rswa_cache_init(desc, A + 2, A, A, check=False) == rs.RSWA_ERR_ALIGN
+
+
+def test_masked_argument_checks():
+    m = lambda **kw: rs.rswa_masked_attn(**{**dict(q=A, k=A, v=A, out=A, seq_len=300, ref_len=40, window=8,
+                                                    num_heads=2, head_dim=128), **kw}, check=False)
+    assert m(q=None) == rs.RSWA_ERR_NULL
+    assert m(ref_len=301) == rs.RSWA_ERR_SHAPE
+    assert m(seq_len=-1) == rs.RSWA_ERR_SHAPE
+    assert m(window=0) == rs.RSWA_ERR_SHAPE
+    assert m(num_heads=0) == rs.RSWA_ERR_SHAPE
+    assert m(head_dim=64) == rs.RSWA_ERR_UNSUPPORTED
+    assert m(dtype=rs.RSWA_FP32) == rs.RSWA_ERR_UNSUPPORTED
+    assert m(prefix_mode=3) == rs.RSWA_ERR_UNSUPPORTED
+    assert m(k=A + 2) == rs.RSWA_ERR_ALIGN
+    assert m(scale=math.nan) == rs.RSWA_ERR_SHAPE
+    assert m(seq_len=0, ref_len=0) == rs.RSWA_OK   # nothing to do, nothing enqueued
+
+
+def test_check_device_error_null_arguments():
+    lib = rs.library()
+    flags = ctypes.c_int32(0)
+    assert lib.rswa_check_device_error(None, ctypes.byref(flags), None) == rs.RSWA_ERR_NULL
+    desc = good_desc()
+    assert lib.rswa_check_device_error(ctypes.byref(desc), None, None) == rs.RSWA_ERR_NULL
