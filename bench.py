@@ -131,6 +131,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the contrast and masked lines")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="first run a plain 1 GiB device copy 3 times (scale reference for HBM counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -148,6 +150,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     rs.library()  # fail loudly if the HIP library is missing
+
+    if args.copy_reference:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     w = wl.FORTY_PAGE
     B, H, d, L, n = w.batch, w.heads, w.head_dim, w.ref_len, w.window
