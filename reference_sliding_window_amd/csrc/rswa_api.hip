@@ -217,7 +217,8 @@ rswa_status_t rswa_masked_attn(const void *q, const void *k, const void *v, void
   if (dtype != RSWA_BF16 || head_dim != 128) return RSWA_ERR_UNSUPPORTED;
   if (prefix_mode != RSWA_PREFIX_CAUSAL && prefix_mode != RSWA_PREFIX_FULL)
     return RSWA_ERR_UNSUPPORTED;
-  if ((int64_t)seq_len * num_heads * head_dim > ((int64_t)1 << 40)) return RSWA_ERR_CAPACITY;
+  // element offsets inside the kernel are 32-bit
+  if ((int64_t)seq_len * num_heads * head_dim >= ((int64_t)1 << 31)) return RSWA_ERR_CAPACITY;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RSWA_ERR_ALIGN;
   if (!isfinite(scale)) return RSWA_ERR_SHAPE;
   if (seq_len == 0) return RSWA_OK;

@@ -14,8 +14,10 @@
 // Memory-bound design: each K/V row of d bf16 values (256 B at d = 128) is
 // read by 16 lanes with one 16-byte load each, so a wave64 load instruction
 // covers 4 consecutive rows = 1 KB contiguous. Every loaded element is used
-// exactly once by the lane that loaded it, so K/V go straight to VGPRs; the
-// 16-lane dot-product reduction uses DPP row operations (no LDS traffic).
+// exactly once by the lane that loaded it, so K/V go straight to VGPRs with
+// non-temporal loads (on MI355X they stream about 12 % faster than ordinary
+// loads: nothing here is re-read); the 16-lane dot-product reduction uses DPP
+// row operations (no LDS traffic).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -27,13 +29,32 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// Native 16-byte vector (HIP's uint4 is a struct whose copies can go through
+// private memory, and the non-temporal builtin does not take it).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+#ifndef RSWA_DECODE_U
+#define RSWA_DECODE_U 8  // 16-byte K and V loads in flight per lane per tile
+#endif
+#ifndef RSWA_DECODE_NT
+#define RSWA_DECODE_NT 1  // stream K/V with non-temporal loads (0: ordinary loads)
+#endif
+
+__device__ __forceinline__ u32x4_t stream_load(const u32x4_t *p) {
+#if RSWA_DECODE_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
 // ------------------------------------------------------------ element types
 struct Bf16 {
   using storage = uint16_t;
   static constexpr int kBytes = 2;
   static constexpr int kPerVec = 8;  // elements per 16-byte vector
-  __device__ static inline void unpack(const uint4 &w, float *f) {
-    const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+  __device__ static inline void unpack(const u32x4_t &w, float *f) {
+    const uint32_t x[4] = {w[0], w[1], w[2], w[3]};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f[2 * i] = __uint_as_float(x[i] << 16);
@@ -53,11 +74,11 @@ struct F32 {
   using storage = float;
   static constexpr int kBytes = 4;
   static constexpr int kPerVec = 4;
-  __device__ static inline void unpack(const uint4 &w, float *f) {
-    f[0] = __uint_as_float(w.x);
-    f[1] = __uint_as_float(w.y);
-    f[2] = __uint_as_float(w.z);
-    f[3] = __uint_as_float(w.w);
+  __device__ static inline void unpack(const u32x4_t &w, float *f) {
+    f[0] = __uint_as_float(w[0]);
+    f[1] = __uint_as_float(w[1]);
+    f[2] = __uint_as_float(w[2]);
+    f[3] = __uint_as_float(w[3]);
   }
 };
 
@@ -137,8 +158,8 @@ __global__ __launch_bounds__(256) void cache_init_kernel(InitParams p) {
   const int nvec = (r1 - r0) * G::kLpr;
   for (int i = threadIdx.x; i < nvec; i += 256) {
     const int64_t off = (int64_t)r0 * D + (int64_t)i * G::kEpl;
-    *reinterpret_cast<uint4 *>(kd + off) = *reinterpret_cast<const uint4 *>(ks + off);
-    *reinterpret_cast<uint4 *>(vd + off) = *reinterpret_cast<const uint4 *>(vs + off);
+    *reinterpret_cast<u32x4_t *>(kd + off) = *reinterpret_cast<const u32x4_t *>(ks + off);
+    *reinterpret_cast<u32x4_t *>(vd + off) = *reinterpret_cast<const u32x4_t *>(vs + off);
   }
 }
 
@@ -169,8 +190,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     const int h = i / G::kLpr, c = i % G::kLpr;
     const int64_t dst = ((int64_t)h * (L + p.window) + slot) * D + c * G::kEpl;
     const int64_t src = (int64_t)h * D + c * G::kEpl;
-    *reinterpret_cast<uint4 *>(kd + dst) = *reinterpret_cast<const uint4 *>(kn + src);
-    *reinterpret_cast<uint4 *>(vd + dst) = *reinterpret_cast<const uint4 *>(vn + src);
+    *reinterpret_cast<u32x4_t *>(kd + dst) = *reinterpret_cast<const u32x4_t *>(kn + src);
+    *reinterpret_cast<u32x4_t *>(vd + dst) = *reinterpret_cast<const u32x4_t *>(vn + src);
   }
   __syncthreads();
   if (threadIdx.x == 0) p.step[b] = T0 + 1;
@@ -236,13 +257,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   if (fused && star >= start && star < end && wave == 0 && lane < kLpr) {
     S *kd = static_cast<S *>(p.k) + head_off + (int64_t)star * D;
     S *vd = static_cast<S *>(p.v) + head_off + (int64_t)star * D;
-    reinterpret_cast<uint4 *>(kd)[lane] = reinterpret_cast<const uint4 *>(kn)[lane];
-    reinterpret_cast<uint4 *>(vd)[lane] = reinterpret_cast<const uint4 *>(vn)[lane];
+    reinterpret_cast<u32x4_t *>(kd)[lane] = reinterpret_cast<const u32x4_t *>(kn)[lane];
+    reinterpret_cast<u32x4_t *>(vd)[lane] = reinterpret_cast<const u32x4_t *>(vn)[lane];
   }
 
   float qf[kEpl];
   {
-    const uint4 qv = reinterpret_cast<const uint4 *>(static_cast<const S *>(p.q) + bh * D)[c];
+    const u32x4_t qv = reinterpret_cast<const u32x4_t *>(static_cast<const S *>(p.q) + bh * D)[c];
     E::unpack(qv, qf);
 #pragma unroll
     for (int e = 0; e < kEpl; ++e) qf[e] *= p.scale_log2;
@@ -254,7 +275,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   for (int e = 0; e < kEpl; ++e) acc[e] = 0.f;
 
   for (int t0 = start + wave * kTile; t0 < end; t0 += kWaves * kTile) {
-    uint4 kr[U], vr[U];
+    u32x4_t kr[U], vr[U];
     bool valid[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -262,12 +283,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
       valid[u] = row < end;
       const int rr = valid[u] ? row : end - 1;
       const bool is_new = (rr == star);
-      const uint4 *kp = is_new ? reinterpret_cast<const uint4 *>(kn)
-                               : reinterpret_cast<const uint4 *>(kb + (int64_t)rr * D);
-      const uint4 *vp = is_new ? reinterpret_cast<const uint4 *>(vn)
-                               : reinterpret_cast<const uint4 *>(vb + (int64_t)rr * D);
-      kr[u] = kp[c];
-      vr[u] = vp[c];
+      const u32x4_t *kp = is_new ? reinterpret_cast<const u32x4_t *>(kn)
+                               : reinterpret_cast<const u32x4_t *>(kb + (int64_t)rr * D);
+      const u32x4_t *vp = is_new ? reinterpret_cast<const u32x4_t *>(vn)
+                               : reinterpret_cast<const u32x4_t *>(vb + (int64_t)rr * D);
+      kr[u] = stream_load(kp + c);
+      vr[u] = stream_load(vp + c);
     }
     float s[U];
     float tmax = kNegInf;
@@ -386,7 +407,7 @@ __global__ void clear_word_kernel(int32_t *w) { *w = 0; }
 
 template <class E, int D>
 hipError_t launch_decode_t(const DecodeParams &p, hipStream_t s) {
-  constexpr int kU = 8;
+  constexpr int kU = RSWA_DECODE_U;
   dim3 grid(p.splits, p.heads, p.batch);
   hipLaunchKernelGGL((decode_split_kernel<E, D, kU>), grid, dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();

@@ -7,28 +7,34 @@
 // causal, or see the whole prefix in RSWA_PREFIX_FULL mode. Softmax and the
 // weighted sum follow Eqs. (3)-(4).
 //
-// Design (one workgroup = 128 query rows of one head, 4 waves x 32 rows):
-//  * Only key blocks that intersect the two-segment mask are visited: the
-//    prefix range [0, min(L_m, q_end)) and the window range
-//    [max(L_m, first_output_row - n + 1), q_end). Only blocks that cut the
-//    mask (partial blocks, the causal diagonal of prefix rows, the window)
-//    evaluate the mask; all other blocks run unmasked.
+// Design (one workgroup = 128 query rows of one head, 4 waves x 32 rows,
+// two workgroups per CU):
+//  * Only the 64-key blocks that intersect the two-segment mask are visited:
+//    the prefix range [0, min(L_m, q_end)) and the window range
+//    [max(L_m, first_output_row - n + 1), q_end). Each wave runs three loops:
+//    prefix blocks that hide no key from any of its queries (no mask code at
+//    all), prefix blocks that cut the mask (partial block, causal diagonal of
+//    prefix rows), and window blocks.
 //  * Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS
 //    as the A operand, the wave's Q rows resident in VGPRs as the B operand),
 //    so lane l owns query l % 32: the softmax row max and sum are in-register
 //    plus one exchange with lane l ^ 32.
 //  * O^T += V^T P^T reuses the S^T accumulators as the B operand after the
-//    exp2 and the packed bf16 convert; V is stored transposed in LDS.
-//  * Keys sit in LDS in a permuted order: with R = block / 16 rows staged per
-//    thread, LDS row rho holds key rho / R + 16 (rho mod R). A thread that
-//    loads keys u, u+16, ... (coalesced rows) then writes them as one packed
-//    word of V^T per d (8 bytes for 64-key blocks, 4 for 32-key blocks).
-//    The contraction over keys does not depend on their order; the mask uses
-//    the true key index.
+//    exp2 and the packed bf16 convert, one 16-key step at a time, so that the
+//    MFMAs of one step overlap the exponentials of the next.
+//  * Keys sit in LDS in a permuted order: LDS row rho of a block holds key
+//    rho / 4 + 16 (rho mod 4), so a thread that loads the coalesced rows
+//    u, u+16, u+32, u+48 writes them as one 8-byte word of V^T per d. Inside
+//    a V^T row, bits 2 and 3 of rho are swapped (the 8 keys an MFMA lane
+//    needs per step become 16 contiguous bytes) and bits 4-5 are XOR-ed with
+//    (d >> 5) to spread the transposing stores over the LDS banks. The
+//    contraction over keys does not depend on their order; the mask uses the
+//    true key index.
 //  * Softmax in base 2 with the scale folded into one FMA before exp2. The
 //    running max used for exponentiation is only raised (and O, l rescaled)
 //    when a block's max exceeds it by more than 8 (a factor 2^8), which keeps
-//    every probability below 2^8 and skips most rescales.
+//    every probability below 2^8 and skips most rescales. The row sum is
+//    taken with v_dot2 over the same bf16 probabilities that enter PV.
 //  * LDS is double buffered: the next block's global loads are issued before
 //    the current block's MFMAs and written to the other buffer after them;
 //    one barrier per block.
@@ -37,6 +43,8 @@
 //    prefix K/V resident in the XCD's L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "rswa_internal.h"
 
@@ -52,27 +60,21 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-#ifndef RSWA_MASKED_BN
-#define RSWA_MASKED_BN 64  // keys per block: 32 or 64
-#endif
-#ifndef RSWA_MASKED_OCC
-#define RSWA_MASKED_OCC 2  // workgroups per CU the register budget is sized for
-#endif
-
 constexpr int kD = 128;           // head dim
 constexpr int kBM = 128;          // query rows per workgroup
-constexpr int kBN = RSWA_MASKED_BN;
-constexpr int kRpt = kBN / 16;    // key rows staged per thread
+constexpr int kBN = 64;           // keys per block
+constexpr int kTiles = kBN / 32;  // 32-key S^T tiles per block
 constexpr int kKPitch = kD + 8;   // LDS row pitch of K (elements)
-constexpr int kVPitch = kBN + 4;  // LDS row pitch of V^T (elements)
-static_assert(kBN == 32 || kBN == 64, "key block of 32 or 64");
+constexpr int kVPitch = kBN + 8;  // LDS row pitch of V^T (elements; rows stay 16-byte aligned)
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleThreshold = 8.f;  // log2 units
 
 struct Buf {
   uint16_t k[kBN * kKPitch];   // K block, [rho][d]
-  uint16_t vt[kD * kVPitch];   // V block transposed, [d][rho]
+  uint16_t vt[kD * kVPitch];   // V block transposed, [d][vt_col]
 };
+
+__device__ constexpr bf16x2_t kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
 
@@ -82,15 +84,38 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 }
 
 // true key offset (within the block) of LDS row rho
-__device__ __forceinline__ int key_of_row(int rho) { return rho / kRpt + 16 * (rho % kRpt); }
+__device__ __forceinline__ int key_of_row(int rho) { return (rho >> 2) + 16 * (rho & 3); }
+
+// Physical V^T column of LDS key row rho in row d (see the header comment).
+__device__ __forceinline__ int vt_col(int d, int rho) {
+  const int swapped = (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
+  return swapped ^ (16 * ((d >> 5) & 3));
+}
+
+// Sets to -inf the scores of keys the two-segment mask hides from query qi.
+// Accumulator element r of tile kt is LDS row rho = 32 kt + 8 (r/4) + 4 hi + r%4.
+template <bool kWindow>
+__device__ __forceinline__ void apply_mask(f32x16_t (&s)[kTiles], int kb0, int kend, int qi, int n,
+                                           bool sees_prefix, int hi) {
+#pragma unroll
+  for (int kt = 0; kt < kTiles; ++kt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rho = kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      const int j = kb0 + key_of_row(rho);
+      const bool vis = kWindow ? (j < kend && j <= qi && qi - j < n)
+                               : (j < kend && (sees_prefix || j <= qi));
+      s[kt][r] = vis ? s[kt][r] : kNegInf;
+    }
+  }
+}
 
 struct Block {
-  int kb0;      // first key of the block
-  int kend;     // end of the key range the block belongs to
-  bool window;  // block of the window range (keys >= L_m)
+  int kb0;   // first key of the block
+  int kend;  // end of the key range the block belongs to
 };
 
-__global__ __launch_bounds__(256, RSWA_MASKED_OCC) void masked_attn_kernel(MaskedParams p) {
+__global__ __launch_bounds__(256, 2) void masked_attn_kernel(MaskedParams p) {
   __shared__ Buf sm[2];
   const int N = p.seq_len, H = p.heads, Lm = p.ref_len, n = p.window;
   const bool full_prefix = p.prefix_mode == RSWA_PREFIX_FULL;
@@ -121,14 +146,15 @@ __global__ __launch_bounds__(256, RSWA_MASKED_OCC) void masked_attn_kernel(Maske
   const int nb_win = (win_hi - win_lo + kBN - 1) / kBN;
   const int nblocks = nb_pre + nb_win;
   auto block_of = [&](int bi) -> Block {
-    if (bi < nb_pre) return {bi * kBN, pre_hi, false};
-    return {win_lo + (bi - nb_pre) * kBN, win_hi, true};
+    if (bi < nb_pre) return {bi * kBN, pre_hi};
+    return {win_lo + (bi - nb_pre) * kBN, win_hi};
   };
 
   // This wave's 32 queries; lane l owns query qi.
   const int qw0 = q0 + wave * 32;
   const int qi = qw0 + l32;
   const bool q_ok = qi < N;
+  const bool sees_prefix = qi >= Lm || full_prefix;  // every prefix key is visible
   bf16x8_t qf[kD / 16];
   {
     const uint16_t *qrow = Qg + (int64_t)(q_ok ? qi : 0) * row_stride;
@@ -146,41 +172,36 @@ __global__ __launch_bounds__(256, RSWA_MASKED_OCC) void masked_attn_kernel(Maske
   float m = kNegInf;  // running max (raw scores) used for exponentiation
   float l = 0.f;      // this lane's part of the row sum
 
-  // Staging: thread t loads keys u + 16 i (i < kRpt), u = t >> 4, 16-byte
-  // column chunk c = t & 15, of K and V.
+  // Staging: thread t loads keys u + 16 i (i = 0..3), u = t >> 4, 16-byte
+  // column chunk c = t & 15, of K and V. Element offsets fit in 32 bits (the
+  // host rejects tensors of 2^31 elements or more).
   const int su = tid >> 4, sc = tid & 15;
-  u32x4_t kst[kRpt], vst[kRpt];
+  const uint32_t stride32 = (uint32_t)row_stride;
+  u32x4_t kst[4], vst[4];
   auto load_block = [&](const Block &bk) {
 #pragma unroll
-    for (int i = 0; i < kRpt; ++i) {
-      int r = bk.kb0 + su + 16 * i;
-      r = r < bk.kend ? r : bk.kend - 1;
-      kst[i] = *reinterpret_cast<const u32x4_t *>(Kg + (int64_t)r * row_stride + sc * 8);
-      vst[i] = *reinterpret_cast<const u32x4_t *>(Vg + (int64_t)r * row_stride + sc * 8);
+    for (int i = 0; i < 4; ++i) {
+      const int r = min(bk.kb0 + su + 16 * i, bk.kend - 1);
+      const uint32_t off = __umul24((uint32_t)r, stride32) + sc * 8;
+      kst[i] = *reinterpret_cast<const u32x4_t *>(Kg + off);
+      vst[i] = *reinterpret_cast<const u32x4_t *>(Vg + off);
     }
   };
+  const int vcol = vt_col(sc * 8, 4 * su);  // same for all 8 d of the thread's chunk
   auto store_block = [&](Buf &b) {
 #pragma unroll
-    for (int i = 0; i < kRpt; ++i)
-      *reinterpret_cast<u32x4_t *>(&b.k[(kRpt * su + i) * kKPitch + sc * 8]) = kst[i];
-    const u32x4_t *v = vst;
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4_t *>(&b.k[(4 * su + i) * kKPitch + sc * 8]) = kst[i];
 #pragma unroll
     for (int k2 = 0; k2 < 4; ++k2) {
       // d = 8 sc + 2 k2 (low halves) and d + 1 (high halves) of keys u + 16 i
       const int d = sc * 8 + 2 * k2;
-      if constexpr (kRpt == 4) {
-        const u32x2_t even = {__builtin_amdgcn_perm(v[1][k2], v[0][k2], 0x05040100u),
-                              __builtin_amdgcn_perm(v[3][k2], v[2][k2], 0x05040100u)};
-        const u32x2_t odd = {__builtin_amdgcn_perm(v[1][k2], v[0][k2], 0x07060302u),
-                             __builtin_amdgcn_perm(v[3][k2], v[2][k2], 0x07060302u)};
-        *reinterpret_cast<u32x2_t *>(&b.vt[d * kVPitch + kRpt * su]) = even;
-        *reinterpret_cast<u32x2_t *>(&b.vt[(d + 1) * kVPitch + kRpt * su]) = odd;
-      } else {
-        *reinterpret_cast<uint32_t *>(&b.vt[d * kVPitch + kRpt * su]) =
-            __builtin_amdgcn_perm(v[1][k2], v[0][k2], 0x05040100u);
-        *reinterpret_cast<uint32_t *>(&b.vt[(d + 1) * kVPitch + kRpt * su]) =
-            __builtin_amdgcn_perm(v[1][k2], v[0][k2], 0x07060302u);
-      }
+      const u32x2_t even = {__builtin_amdgcn_perm(vst[1][k2], vst[0][k2], 0x05040100u),
+                            __builtin_amdgcn_perm(vst[3][k2], vst[2][k2], 0x05040100u)};
+      const u32x2_t odd = {__builtin_amdgcn_perm(vst[1][k2], vst[0][k2], 0x07060302u),
+                           __builtin_amdgcn_perm(vst[3][k2], vst[2][k2], 0x07060302u)};
+      *reinterpret_cast<u32x2_t *>(&b.vt[d * kVPitch + vcol]) = even;
+      *reinterpret_cast<u32x2_t *>(&b.vt[(d + 1) * kVPitch + vcol]) = odd;
     }
   };
 
@@ -189,48 +210,32 @@ __global__ __launch_bounds__(256, RSWA_MASKED_OCC) void masked_attn_kernel(Maske
     load_block(block_of(0));
     store_block(sm[0]);
   }
-  for (int bi = 0; bi < nblocks; ++bi) {
+
+  // One key block. kMode 0: no key of the block is hidden from any query of
+  // the wave; 1: prefix block that cuts the mask (partial block, or the causal
+  // diagonal of prefix rows); 2: window block.
+  auto body = [&](int bi, auto mode) {
+    constexpr int kMode = decltype(mode)::value;
     const Block bk = block_of(bi);
     __syncthreads();  // sm[bi & 1] is complete; sm[(bi + 1) & 1] is no longer read
     const bool has_next = bi + 1 < nblocks;
     if (has_next) load_block(block_of(bi + 1));
     const Buf &b = sm[bi & 1];
 
-    // S^T tiles: kBN / 32 x (32 keys x 32 queries)
-    constexpr int kTiles = kBN / 32;
+    // S^T tiles: kTiles x (32 keys x 32 queries)
     f32x16_t s[kTiles];
 #pragma unroll
     for (int kt = 0; kt < kTiles; ++kt) {
-      s[kt] = f32x16_t{};
       const uint16_t *krow = &b.k[(kt * 32 + l32) * kKPitch + hi * 8];
 #pragma unroll
       for (int ks = 0; ks < kD / 16; ++ks) {
         const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t *>(krow + ks * 16));
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kt], 0, 0, 0);
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? f32x16_t{} : s[kt],
+                                                        0, 0, 0);
       }
     }
-
-    // Does this block cut the mask for any query of the wave? (wave-uniform)
-    const bool partial = bk.kb0 + kBN > bk.kend;
-    const bool diag = !full_prefix && qw0 < Lm && qw0 < bk.kb0 + kBN - 1;
-    if (bk.window || partial || diag) {
-      // Accumulator element r of tile kt is LDS row rho = 32 kt + 8 (r/4) + 4 hi + r%4.
-#pragma unroll
-      for (int kt = 0; kt < kTiles; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rho = kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const int j = bk.kb0 + key_of_row(rho);
-          bool vis = j < bk.kend;
-          if (bk.window) {
-            vis = vis && j <= qi && qi - j < n;
-          } else {
-            vis = vis && (qi >= Lm || full_prefix || j <= qi);
-          }
-          s[kt][r] = vis ? s[kt][r] : kNegInf;
-        }
-      }
-    }
+    if constexpr (kMode == 1) apply_mask<false>(s, bk.kb0, bk.kend, qi, n, sees_prefix, hi);
+    if constexpr (kMode == 2) apply_mask<true>(s, bk.kb0, bk.kend, qi, n, sees_prefix, hi);
 
     float bmax = kNegInf;
 #pragma unroll
@@ -250,40 +255,49 @@ __global__ __launch_bounds__(256, RSWA_MASKED_OCC) void masked_attn_kernel(Maske
     }
     const float mc = (m == kNegInf) ? 0.f : m * c;
 
-    // P^T as bf16 B operands: step (kt, half) uses accumulator elements
-    // 8 half .. 8 half + 7 (LDS rows 32 kt + 16 half + {4 hi.., 8 + 4 hi..}).
-    bf16x8_t pb[2 * kTiles];
+    // Per 16-key step st = 2 kt + half: P^T as a bf16 B operand from accumulator
+    // elements 8 half .. 8 half + 7 of tile kt (LDS rows 32 kt + 16 half +
+    // {4 hi.., 8 + 4 hi..}), then O^T[d][q] += V^T[d][rho] P^T[rho][q] for the
+    // four 32-row d blocks.
 #pragma unroll
-    for (int kt = 0; kt < kTiles; ++kt) {
+    for (int st = 0; st < 2 * kTiles; ++st) {
+      const int kt = st >> 1, half = st & 1;
+      uint32_t w4[4];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        uint32_t w4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * half + 2 * e], c, -mc));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * half + 2 * e + 1], c, -mc));
-          l += p0 + p1;
-          w4[e] = pack_bf16(p0, p1);
-        }
-        pb[2 * kt + half] = as_bf16x8(u32x4_t{w4[0], w4[1], w4[2], w4[3]});
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * half + 2 * e], c, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * half + 2 * e + 1], c, -mc));
+        w4[e] = pack_bf16(p0, p1);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w4[e]), kOnes, l, false);
       }
-    }
-
-    // O^T[d][q] += V^T[d][rho] P^T[rho][q]
+      const bf16x8_t pb = as_bf16x8(u32x4_t{w4[0], w4[1], w4[2], w4[3]});
 #pragma unroll
-    for (int db = 0; db < kD / 32; ++db) {
-      const uint16_t *vrow = &b.vt[(db * 32 + l32) * kVPitch + 4 * hi];
-#pragma unroll
-      for (int st = 0; st < 2 * kTiles; ++st) {
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vrow + 16 * st);
-        const u32x2_t hi8 = *reinterpret_cast<const u32x2_t *>(vrow + 16 * st + 8);
-        const bf16x8_t a = as_bf16x8(u32x4_t{lo.x, lo.y, hi8.x, hi8.y});
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], o[db], 0, 0, 0);
+      for (int db = 0; db < kD / 32; ++db) {
+        // vt_col(d, 16 st + 4 hi) = (16 st ^ 16 db) + 8 hi for every d of this
+        // d block: one 16-byte read at a compile-time offset from a lane base
+        const uint16_t *vrow = &b.vt[(db * 32 + l32) * kVPitch + 8 * hi];
+        const bf16x8_t a =
+            as_bf16x8(*reinterpret_cast<const u32x4_t *>(vrow + ((16 * st) ^ (16 * db))));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
       }
     }
 
     if (has_next) store_block(sm[(bi + 1) & 1]);
-  }
+  };
+
+  // Prefix blocks [0, nb_clear) hide no key from any query of this wave: they
+  // are whole and, for causal prefix rows, lie left of the wave's diagonal.
+  // Different waves may split differently; every wave still runs nblocks
+  // iterations, hence the same barriers.
+  int nb_clear = pre_hi / kBN;
+  if (!full_prefix && qw0 < Lm) nb_clear = min(nb_clear, (qw0 + 1) / kBN);
+  // Drain every outstanding load (the Q fragments among them) before the loop,
+  // so that the loop's waits only cover the block prefetch.
+  __builtin_amdgcn_s_waitcnt(0);
+  int bi = 0;
+  for (; bi < nb_clear; ++bi) body(bi, std::integral_constant<int, 0>{});
+  for (; bi < nb_pre; ++bi) body(bi, std::integral_constant<int, 1>{});
+  for (; bi < nblocks; ++bi) body(bi, std::integral_constant<int, 2>{});
 
   // Normalise and store: accumulator element r of o[db] is d = 32 db + 8 (r/4) + 4 hi + r%4.
   l += __shfl_xor(l, 32, 64);
