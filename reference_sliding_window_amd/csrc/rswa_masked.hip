@@ -15,29 +15,24 @@
 //    prefix blocks that hide no key from any of its queries (no mask code at
 //    all), prefix blocks that cut the mask (partial block, causal diagonal of
 //    prefix rows), and window blocks.
-//  * Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS
-//    as the A operand, the wave's Q rows resident in VGPRs as the B operand),
-//    so lane l owns query l % 32: the softmax row max and sum are in-register
-//    plus one exchange with lane l ^ 32.
+//  * K and V blocks go from global memory straight into LDS by DMA
+//    (global_load_lds_dwordx4), double buffered: the next block is in flight
+//    while the current one is multiplied; one barrier per block. Tiles are
+//    row-major with 256-byte rows and XOR-swizzled 16-byte chunks, so the
+//    fragment reads below are free of bank conflicts.
+//  * Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K fragments
+//    from LDS as the A operand, the wave's Q rows resident in VGPRs as the B
+//    operand), so lane l owns query l % 32: the softmax row max and sum are
+//    in-register plus one exchange with lane l ^ 32.
 //  * O^T += V^T P^T reuses the S^T accumulators as the B operand after the
-//    exp2 and the packed bf16 convert, one 16-key step at a time, so that the
-//    MFMAs of one step overlap the exponentials of the next.
-//  * Keys sit in LDS in a permuted order: LDS row rho of a block holds key
-//    rho / 4 + 16 (rho mod 4), so a thread that loads the coalesced rows
-//    u, u+16, u+32, u+48 writes them as one 8-byte word of V^T per d. Inside
-//    a V^T row, bits 2 and 3 of rho are swapped (the 8 keys an MFMA lane
-//    needs per step become 16 contiguous bytes) and bits 4-5 are XOR-ed with
-//    (d >> 5) to spread the transposing stores over the LDS banks. The
-//    contraction over keys does not depend on their order; the mask uses the
-//    true key index.
+//    exp2 and the packed bf16 convert, one 16-key step at a time; the V^T A
+//    operand comes from the row-major V tile through transposing LDS reads
+//    (ds_read_b64_tr_b16, two per operand).
 //  * Softmax in base 2 with the scale folded into one FMA before exp2. The
 //    running max used for exponentiation is only raised (and O, l rescaled)
 //    when a block's max exceeds it by more than 8 (a factor 2^8), which keeps
 //    every probability below 2^8 and skips most rescales. The row sum is
 //    taken with v_dot2 over the same bf16 probabilities that enter PV.
-//  * LDS is double buffered: the next block's global loads are issued before
-//    the current block's MFMAs and written to the other buffer after them;
-//    one barrier per block.
 //  * Workgroups are ordered so that all query blocks of a head run on the same
 //    XCD (hardware places workgroup i on XCD i mod 8), keeping that head's
 //    prefix K/V resident in the XCD's L2.
@@ -64,15 +59,24 @@ constexpr int kD = 128;           // head dim
 constexpr int kBM = 128;          // query rows per workgroup
 constexpr int kBN = 64;           // keys per block
 constexpr int kTiles = kBN / 32;  // 32-key S^T tiles per block
-constexpr int kKPitch = kD + 8;   // LDS row pitch of K (elements)
-constexpr int kVPitch = kBN + 8;  // LDS row pitch of V^T (elements; rows stay 16-byte aligned)
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleThreshold = 8.f;  // log2 units
+constexpr int kRowBytes = kD * 2;         // 256-byte K and V rows in LDS, no padding
 
+// K and V blocks, row-major, rows = LDS key rows; 16-byte chunks swizzled (see chunk_swz).
 struct Buf {
-  uint16_t k[kBN * kKPitch];   // K block, [rho][d]
-  uint16_t vt[kD * kVPitch];   // V block transposed, [d][vt_col]
+  uint16_t k[kBN * kD];
+  uint16_t v[kBN * kD];
 };
+
+// Physical 16-byte chunk of logical chunk c in row r: c ^ (4 (r mod 4) + (r / 4) mod 4).
+// Eight consecutive rows read at one chunk (K fragments) and four consecutive rows
+// read at four neighbouring chunks (transposing V reads) then hit distinct banks.
+__device__ __forceinline__ int chunk_swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ constexpr bf16x2_t kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -81,15 +85,6 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t u) { return __builtin_bit_
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   const f32x2_t f = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-}
-
-// true key offset (within the block) of LDS row rho
-__device__ __forceinline__ int key_of_row(int rho) { return (rho >> 2) + 16 * (rho & 3); }
-
-// Physical V^T column of LDS key row rho in row d (see the header comment).
-__device__ __forceinline__ int vt_col(int d, int rho) {
-  const int swapped = (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
-  return swapped ^ (16 * ((d >> 5) & 3));
 }
 
 // Sets to -inf the scores of keys the two-segment mask hides from query qi.
@@ -102,7 +97,7 @@ __device__ __forceinline__ void apply_mask(f32x16_t (&s)[kTiles], int kb0, int k
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int rho = kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      const int j = kb0 + key_of_row(rho);
+      const int j = kb0 + rho;
       const bool vis = kWindow ? (j < kend && j <= qi && qi - j < n)
                                : (j < kend && (sees_prefix || j <= qi));
       s[kt][r] = vis ? s[kt][r] : kNegInf;
@@ -172,44 +167,55 @@ __global__ __launch_bounds__(256, 2) void masked_attn_kernel(MaskedParams p) {
   float m = kNegInf;  // running max (raw scores) used for exponentiation
   float l = 0.f;      // this lane's part of the row sum
 
-  // Staging: thread t loads keys u + 16 i (i = 0..3), u = t >> 4, 16-byte
-  // column chunk c = t & 15, of K and V. Element offsets fit in 32 bits (the
-  // host rejects tensors of 2^31 elements or more).
-  const int su = tid >> 4, sc = tid & 15;
+  // Global -> LDS by DMA (global_load_lds_dwordx4: lane L's 16 bytes land at the
+  // wave-uniform LDS base + 16 L). Wave w fills rows 16 w .. 16 w + 15 of the K and
+  // V tiles with 4 instructions each; instruction j covers rows 16 w + 4 j + L / 16,
+  // physical chunk L % 16, i.e. logical chunk (L % 16) ^ chunk_swz(row).
+  // Element offsets fit in 32 bits (the host rejects tensors of 2^31 elements or more).
   const uint32_t stride32 = (uint32_t)row_stride;
-  u32x4_t kst[4], vst[4];
-  auto load_block = [&](const Block &bk) {
+  int dma_row[4];
+  uint32_t dma_col[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = min(bk.kb0 + su + 16 * i, bk.kend - 1);
-      const uint32_t off = __umul24((uint32_t)r, stride32) + sc * 8;
-      kst[i] = *reinterpret_cast<const u32x4_t *>(Kg + off);
-      vst[i] = *reinterpret_cast<const u32x4_t *>(Vg + off);
+  for (int j = 0; j < 4; ++j) {
+    dma_row[j] = 16 * wave + 4 * j + (lane >> 4);
+    dma_col[j] = 8u * (uint32_t)((lane & 15) ^ chunk_swz(dma_row[j]));
+  }
+  auto dma_block = [&](const Block &bk, Buf &b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = min(bk.kb0 + dma_row[j], bk.kend - 1);
+      const uint32_t off = __umul24((uint32_t)r, stride32) + dma_col[j];
+      char *kdst = reinterpret_cast<char *>(b.k) + (16 * wave + 4 * j) * kRowBytes;
+      char *vdst = reinterpret_cast<char *>(b.v) + (16 * wave + 4 * j) * kRowBytes;
+      __builtin_amdgcn_global_load_lds(Kg + off, (lds_void_t *)kdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Vg + off, (lds_void_t *)vdst, 16, 0, 0);
     }
   };
-  const int vcol = vt_col(sc * 8, 4 * su);  // same for all 8 d of the thread's chunk
-  auto store_block = [&](Buf &b) {
+  // K fragment of step ks for S^T tile 0: row l32, logical chunk 2 ks + hi.
+  uint32_t koff[kD / 16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4_t *>(&b.k[(4 * su + i) * kKPitch + sc * 8]) = kst[i];
+  for (int ks = 0; ks < kD / 16; ++ks)
+    koff[ks] = l32 * kRowBytes + 16 * ((2 * ks + hi) ^ chunk_swz(l32));
+  // Transposing V reads: the A operand of 16-key step st and d block db is two
+  // ds_read_b64_tr_b16. In each, lane s addresses row 16 st + 8 h2 + 4 (G / 2) + e,
+  // d = 32 db + 16 (G % 2) + 4 q (G = s / 16, e = s / 4 mod 4, q = s mod 4) and
+  // lane i of each 16-lane group receives d = 32 db + l % 32 of the four rows
+  // base + e; the row-dependent part of the swizzle does not depend on st.
+  uint32_t voff[kD / 32][2];
+  {
+    const int G = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
 #pragma unroll
-    for (int k2 = 0; k2 < 4; ++k2) {
-      // d = 8 sc + 2 k2 (low halves) and d + 1 (high halves) of keys u + 16 i
-      const int d = sc * 8 + 2 * k2;
-      const u32x2_t even = {__builtin_amdgcn_perm(vst[1][k2], vst[0][k2], 0x05040100u),
-                            __builtin_amdgcn_perm(vst[3][k2], vst[2][k2], 0x05040100u)};
-      const u32x2_t odd = {__builtin_amdgcn_perm(vst[1][k2], vst[0][k2], 0x07060302u),
-                           __builtin_amdgcn_perm(vst[3][k2], vst[2][k2], 0x07060302u)};
-      *reinterpret_cast<u32x2_t *>(&b.vt[d * kVPitch + vcol]) = even;
-      *reinterpret_cast<u32x2_t *>(&b.vt[(d + 1) * kVPitch + vcol]) = odd;
-    }
-  };
+    for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int row = 8 * h2 + 4 * (G >> 1) + e;
+        const int chunk = (4 * db + 2 * (G & 1) + (q >> 1)) ^ chunk_swz(row);
+        voff[db][h2] = row * kRowBytes + 16 * chunk + 8 * (q & 1);
+      }
+  }
 
   const float c = p.scale_log2;
-  if (nblocks > 0) {
-    load_block(block_of(0));
-    store_block(sm[0]);
-  }
+  if (nblocks > 0) dma_block(block_of(0), sm[0]);
 
   // One key block. kMode 0: no key of the block is hidden from any query of
   // the wave; 1: prefix block that cuts the mask (partial block, or the causal
@@ -217,19 +223,24 @@ __global__ __launch_bounds__(256, 2) void masked_attn_kernel(MaskedParams p) {
   auto body = [&](int bi, auto mode) {
     constexpr int kMode = decltype(mode)::value;
     const Block bk = block_of(bi);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA into sm[bi & 1] landed
     __syncthreads();  // sm[bi & 1] is complete; sm[(bi + 1) & 1] is no longer read
     const bool has_next = bi + 1 < nblocks;
-    if (has_next) load_block(block_of(bi + 1));
+    if (has_next) dma_block(block_of(bi + 1), sm[(bi + 1) & 1]);
     const Buf &b = sm[bi & 1];
+    // let the scheduler interleave the LDS fragment reads with the MFMAs
+    __builtin_amdgcn_iglp_opt(0);
+    const char *kb = reinterpret_cast<const char *>(b.k);
+    const char *vb = reinterpret_cast<const char *>(b.v);
 
     // S^T tiles: kTiles x (32 keys x 32 queries)
     f32x16_t s[kTiles];
 #pragma unroll
     for (int kt = 0; kt < kTiles; ++kt) {
-      const uint16_t *krow = &b.k[(kt * 32 + l32) * kKPitch + hi * 8];
 #pragma unroll
       for (int ks = 0; ks < kD / 16; ++ks) {
-        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t *>(krow + ks * 16));
+        const bf16x8_t a = as_bf16x8(
+            *reinterpret_cast<const u32x4_t *>(kb + koff[ks] + kt * 32 * kRowBytes));
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? f32x16_t{} : s[kt],
                                                         0, 0, 0);
       }
@@ -273,16 +284,16 @@ __global__ __launch_bounds__(256, 2) void masked_attn_kernel(MaskedParams p) {
       const bf16x8_t pb = as_bf16x8(u32x4_t{w4[0], w4[1], w4[2], w4[3]});
 #pragma unroll
       for (int db = 0; db < kD / 32; ++db) {
-        // vt_col(d, 16 st + 4 hi) = (16 st ^ 16 db) + 8 hi for every d of this
-        // d block: one 16-byte read at a compile-time offset from a lane base
-        const uint16_t *vrow = &b.vt[(db * 32 + l32) * kVPitch + 8 * hi];
-        const bf16x8_t a =
-            as_bf16x8(*reinterpret_cast<const u32x4_t *>(vrow + ((16 * st) ^ (16 * db))));
+        const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t *)(vb + voff[db][0] + 16 * st * kRowBytes));
+        const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t *)(vb + voff[db][1] + 16 * st * kRowBytes));
+        const u32x2_t a0 = __builtin_bit_cast(u32x2_t, v0), a1 = __builtin_bit_cast(u32x2_t, v1);
+        const bf16x8_t a = as_bf16x8(u32x4_t{a0.x, a0.y, a1.x, a1.y});
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
       }
     }
 
-    if (has_next) store_block(sm[(bi + 1) & 1]);
   };
 
   // Prefix blocks [0, nb_clear) hide no key from any query of this wave: they
