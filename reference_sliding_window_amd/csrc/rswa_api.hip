@@ -46,9 +46,9 @@ bool verbose() {
 }  // namespace
 
 SplitPlan plan_decode_splits(int32_t batch, int32_t heads, int32_t max_len, int32_t requested) {
-  // Default: enough workgroups to give every one of the 256 CUs several
-  // resident workgroups (>= 2048 in total), but never chunks below 64 slots.
-  constexpr int64_t kTargetWorkgroups = 2048;
+  // Default: about 4 workgroups per CU (1024 over the 256 CUs) -- where a plain
+  // non-temporal read stream peaks on MI355X -- but never chunks below 64 slots.
+  constexpr int64_t kTargetWorkgroups = 1024;
   constexpr int32_t kMinChunk = 64;
   const int64_t bh = (int64_t)batch * heads;
   const int32_t len = max_len > 0 ? max_len : 1;
