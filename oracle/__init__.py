@@ -16,5 +16,6 @@ from .rswa import (  # noqa: F401
     reference_segment, decode_window, visible_positions, attend, decode_output,
     cache_size_mha, cache_size_rswa, cache_ratio, FifoCache, ring_slot, ring_image,
     simulate_decode, masked_visible_columns, masked_attention_rows,
+    masked_logsumexp_rows, masked_attention_backward,
     PREFIX_CAUSAL, PREFIX_FULL,
 )

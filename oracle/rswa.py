@@ -209,3 +209,57 @@ def masked_attention_rows(Q, K, V, rows, L_m: int, n: int, scale: float,
         for h in range(H):
             out[r, h] = attend(qi[h], Kc[:, h], Vc[:, h], scale)
     return out
+
+
+# ------------------------------------------- packed form: log-sum-exp and backward
+def masked_logsumexp_rows(Q, K, rows, L_m: int, n: int, scale: float,
+                          prefix_mode: int = PREFIX_CAUSAL) -> np.ndarray:
+    """Natural-log normaliser of each selected row's softmax (Eq. (3)'s denominator):
+    lse_i = log sum_{j visible} exp(scale q_i.k_j). Returns [len(rows)][H] float64."""
+    H = Q.shape[1]
+    out = np.empty((len(rows), H), dtype=np.float64)
+    for r, i in enumerate(rows):
+        cols = np.asarray(masked_visible_columns(int(i), L_m, n, prefix_mode))
+        Kc = np.asarray(K[cols], dtype=np.float64)
+        qi = np.asarray(Q[i], dtype=np.float64)
+        for h in range(H):
+            s = (Kc[:, h] @ qi[h]) * scale
+            mx = s.max()
+            out[r, h] = mx + np.log(np.exp(s - mx).sum())
+    return out
+
+
+def masked_attention_backward(Q, K, V, dO, L_m: int, n: int, scale: float,
+                              prefix_mode: int = PREFIX_CAUSAL, rows=None):
+    """Gradients of the packed forward (Eqs. (3)-(4)) for the loss sum(dO * O).
+
+    For each row i with visible set J(i), p = softmax(scale K_J q_i), o_i = p V_J:
+      dV_j += p_j dO_i;   dP_j = dO_i . v_j;   D_i = dO_i . o_i = sum_j p_j dP_j;
+      dS_j = p_j (dP_j - D_i);   dQ_i = scale sum_j dS_j k_j;   dK_j += scale dS_j q_i.
+    rows: the query rows whose contributions are included (default all). Returns
+    (dQ [len(rows)][H][d] for those rows, dK [N][H][d], dV [N][H][d]) in float64;
+    dK and dV are exact only when rows covers every row that sees the key.
+    """
+    N, H, d = Q.shape
+    rows = range(N) if rows is None else rows
+    dQ = np.zeros((len(rows), H, d))
+    dK = np.zeros((N, H, d))
+    dV = np.zeros((N, H, d))
+    for r, i in enumerate(rows):
+        cols = np.asarray(masked_visible_columns(int(i), L_m, n, prefix_mode))
+        for h in range(H):
+            q = np.asarray(Q[i, h], np.float64)
+            Kc = np.asarray(K[cols, h], np.float64)
+            Vc = np.asarray(V[cols, h], np.float64)
+            g = np.asarray(dO[i, h], np.float64)
+            s = (Kc @ q) * scale
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            o = p @ Vc
+            dP = Vc @ g
+            D = g @ o
+            dS = p * (dP - D)
+            dQ[r, h] = scale * (dS @ Kc)
+            dK[cols, h] += scale * np.outer(dS, q)
+            dV[cols, h] += np.outer(p, g)
+    return dQ, dK, dV

@@ -362,3 +362,54 @@ def test_oracle_package_exports():
     for name in ("visible_positions", "decode_output", "masked_attention_rows", "FifoCache",
                  "ring_image", "cache_ratio"):
         assert hasattr(oracle, name)
+
+
+# ------------------------------------------------------ packed backward and normaliser
+def _torch_masked_grads(Q, K, V, dO, L_m, n, scale, mode):
+    """torch autograd through its own float64 attention with a band-built mask."""
+    N, H, d = Q.shape
+    ones = np.ones((N, N), bool)
+    col_is_ref = np.zeros((N, N), bool)
+    col_is_ref[:, :L_m] = True
+    mask = np.tril(ones) & (col_is_ref | np.triu(ones, -(n - 1)))
+    if mode == orc.PREFIX_FULL:
+        row_is_ref = np.zeros((N, N), bool)
+        row_is_ref[:L_m, :] = True
+        mask = np.where(row_is_ref, col_is_ref, mask)
+    t = [torch.tensor(x.transpose(1, 0, 2), dtype=torch.float64, requires_grad=True) for x in (Q, K, V)]
+    out = F.scaled_dot_product_attention(t[0][None], t[1][None], t[2][None],
+                                         attn_mask=torch.from_numpy(mask)[None, None], scale=scale)[0]
+    out.backward(torch.tensor(dO.transpose(1, 0, 2)))
+    lse = torch.logsumexp((t[0] @ t[1].transpose(1, 2)) * scale
+                          + torch.where(torch.from_numpy(mask), 0.0, -torch.inf), dim=-1)
+    return [x.grad.numpy().transpose(1, 0, 2) for x in t], lse.detach().numpy().T
+
+
+@pytest.mark.parametrize("mode", [orc.PREFIX_CAUSAL, orc.PREFIX_FULL])
+def test_backward_matches_torch_autograd(mode):
+    N, L_m, n, H, d = 19, 6, 4, 2, 5
+    Q, K, V, dO = (_rand((N, H, d), s) for s in (40, 41, 42, 43))
+    dQ, dK, dV = orc.masked_attention_backward(Q, K, V, dO, L_m, n, 0.6, mode)
+    (tq, tk, tv), lse = _torch_masked_grads(Q, K, V, dO, L_m, n, 0.6, mode)
+    np.testing.assert_allclose(dQ, tq, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dK, tk, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dV, tv, rtol=1e-10, atol=1e-12)
+    got = orc.masked_logsumexp_rows(Q, K, range(N), L_m, n, 0.6, mode)
+    np.testing.assert_allclose(got, lse, rtol=1e-12, atol=1e-12)
+
+
+def test_backward_column_sums():
+    """sum_j dV_j = sum_i dO_i (rows of the softmax sum to 1); sum_j dK_j = 0."""
+    N, L_m, n, H, d = 23, 7, 3, 2, 4
+    Q, K, V, dO = (_rand((N, H, d), s) for s in (44, 45, 46, 47))
+    _, dK, dV = orc.masked_attention_backward(Q, K, V, dO, L_m, n, 0.5)
+    np.testing.assert_allclose(dV.sum(0), dO.sum(0), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dK.sum(0), 0.0, atol=1e-12)
+
+
+def test_backward_row_subset_dq():
+    N, L_m, n, H, d = 17, 5, 3, 1, 4
+    Q, K, V, dO = (_rand((N, H, d), s) for s in (48, 49, 50, 51))
+    full, _, _ = orc.masked_attention_backward(Q, K, V, dO, L_m, n, 0.7)
+    part, _, _ = orc.masked_attention_backward(Q, K, V, dO, L_m, n, 0.7, rows=[3, 11, 16])
+    np.testing.assert_allclose(part, full[[3, 11, 16]], rtol=1e-14)
