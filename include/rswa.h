@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RSWA_ABI_VERSION 1
+#define RSWA_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define RSWA_API __attribute__((visibility("default")))
@@ -175,11 +175,50 @@ RSWA_API rswa_status_t rswa_decode_attn(const rswa_cache_t *cache, const void *q
  * bf16 (row-major, heads interleaved). Only RSWA_BF16 and head_dim 128 are
  * implemented. QK^T and PV run on bf16 matrix cores with fp32 accumulation;
  * the probabilities are rounded to bf16 before the PV product.
+ * lse: NULL, or device float [num_heads][seq_len] receiving each row's natural
+ * log of the softmax normaliser, log sum_j exp(scale q_i.k_j) over the visible
+ * keys (the input the backward pass needs).
  */
 RSWA_API rswa_status_t rswa_masked_attn(const void *q, const void *k, const void *v, void *out,
-                               int32_t seq_len, int32_t ref_len, int32_t window,
+                               float *lse, int32_t seq_len, int32_t ref_len, int32_t window,
                                int32_t num_heads, int32_t head_dim, int32_t dtype,
                                int32_t prefix_mode, float scale, void *stream);
+
+/*
+ * Bytes of device workspace rswa_masked_attn_bwd needs for seq_len rows and
+ * num_heads heads (two float arrays [num_heads][roundup(seq_len, 32)]). 0 for
+ * invalid sizes.
+ */
+RSWA_API size_t rswa_masked_bwd_workspace_size(int32_t seq_len, int32_t num_heads);
+
+/*
+ * Backward of rswa_masked_attn for the loss sum(dout * out): the gradients of
+ * O_i = softmax(scale K_J q_i) V_J over the same visible sets J(i) (WeThinkIn
+ * page, Eqs. (1)-(4), the packed reading described at rswa_masked_attn):
+ *   dV_j = sum_i P_ij dO_i,  dS_ij = P_ij (dO_i . v_j - dO_i . O_i),
+ *   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i.
+ * The softmax weights P are recomputed from lse.
+ *
+ *  q, k, v, out, dout  device [seq_len][num_heads][head_dim] bf16; out and lse
+ *               are the forward's outputs for the same q, k, v, sizes, mode
+ *               and scale (other values give gradients of nothing defined).
+ *  lse          device float [num_heads][seq_len] from rswa_masked_attn.
+ *  dq, dk, dv   device [seq_len][num_heads][head_dim] bf16, written whole
+ *               (keys no row sees get zero). Must not alias the inputs.
+ *  workspace    device, 16-byte aligned, >= rswa_masked_bwd_workspace_size
+ *               bytes; its contents on entry do not matter.
+ * Same restrictions as the forward (RSWA_BF16, head_dim 128). Matrix products
+ * run on bf16 matrix cores with fp32 accumulation; P and dS are rounded to
+ * bf16 as operands. Results do not depend on the launch beyond that: the
+ * kernels use no atomics.
+ */
+RSWA_API rswa_status_t rswa_masked_attn_bwd(const void *q, const void *k, const void *v,
+                                   const void *out, const void *dout, const float *lse,
+                                   void *dq, void *dk, void *dv, int32_t seq_len,
+                                   int32_t ref_len, int32_t window, int32_t num_heads,
+                                   int32_t head_dim, int32_t dtype, int32_t prefix_mode,
+                                   float scale, void *workspace, size_t workspace_bytes,
+                                   void *stream);
 
 /*
  * Synchronise `stream`, read the cache's device error word into *flags

@@ -42,7 +42,7 @@ RSWA_DEVERR_ALIGN = 8
 
 EXPORTED = ("rswa_abi_version", "rswa_status_str", "rswa_cache_init", "rswa_append_kv",
             "rswa_decode_workspace_size", "rswa_decode_attn", "rswa_masked_attn",
-            "rswa_check_device_error")
+            "rswa_masked_bwd_workspace_size", "rswa_masked_attn_bwd", "rswa_check_device_error")
 
 
 class RswaError(RuntimeError):
@@ -87,7 +87,10 @@ def _lib() -> ctypes.CDLL:
             "rswa_append_kv": (I32, [D, P, P, P, P]),
             "rswa_decode_workspace_size": (SZ, [D, I32]),
             "rswa_decode_attn": (I32, [D, P, P, P, P, F, I32, P, SZ, P]),
-            "rswa_masked_attn": (I32, [P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, P]),
+            "rswa_masked_attn": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, P]),
+            "rswa_masked_bwd_workspace_size": (SZ, [I32, I32]),
+            "rswa_masked_attn_bwd": (I32, [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
+                                           I32, F, P, SZ, P]),
             "rswa_check_device_error": (I32, [D, ctypes.POINTER(I32), P]),
         }
         for name, (res, args) in sig.items():
@@ -167,10 +170,30 @@ def rswa_decode_attn(desc: CacheDesc, q, out, k_new=None, v_new=None, scale: flo
 
 def rswa_masked_attn(q, k, v, out, seq_len: int, ref_len: int, window: int, num_heads: int,
                      head_dim: int, dtype: int = RSWA_BF16, prefix_mode: int = RSWA_PREFIX_CAUSAL,
-                     scale: float = 0.0, stream=None, check=True) -> int:
-    st = _lib().rswa_masked_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), seq_len, ref_len, window,
-                                 num_heads, head_dim, dtype, prefix_mode, float(scale), _stream(stream))
+                     scale: float = 0.0, stream=None, check=True, lse=None) -> int:
+    st = _lib().rswa_masked_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), seq_len, ref_len,
+                                 window, num_heads, head_dim, dtype, prefix_mode, float(scale),
+                                 _stream(stream))
     return _check(st, "rswa_masked_attn") if check else st
+
+
+def rswa_masked_bwd_workspace_size(seq_len: int, num_heads: int) -> int:
+    return _lib().rswa_masked_bwd_workspace_size(seq_len, num_heads)
+
+
+def rswa_masked_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, seq_len: int, ref_len: int,
+                         window: int, num_heads: int, head_dim: int, dtype: int = RSWA_BF16,
+                         prefix_mode: int = RSWA_PREFIX_CAUSAL, scale: float = 0.0,
+                         workspace=None, workspace_bytes: int | None = None, stream=None,
+                         check=True) -> int:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    st = _lib().rswa_masked_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), seq_len, ref_len, window,
+                                     num_heads, head_dim, dtype, prefix_mode, float(scale),
+                                     _ptr(workspace), int(workspace_bytes), _stream(stream))
+    return _check(st, "rswa_masked_attn_bwd") if check else st
 
 
 def rswa_check_device_error(desc: CacheDesc, stream=None) -> int:

@@ -208,7 +208,7 @@ rswa_status_t rswa_decode_attn(const rswa_cache_t *cache, const void *q, void *o
 }
 
 rswa_status_t rswa_masked_attn(const void *q, const void *k, const void *v, void *out,
-                               int32_t seq_len, int32_t ref_len, int32_t window,
+                               float *lse, int32_t seq_len, int32_t ref_len, int32_t window,
                                int32_t num_heads, int32_t head_dim, int32_t dtype,
                                int32_t prefix_mode, float scale, void *stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return RSWA_ERR_NULL;
@@ -220,6 +220,7 @@ rswa_status_t rswa_masked_attn(const void *q, const void *k, const void *v, void
   // element offsets inside the kernel are 32-bit
   if ((int64_t)seq_len * num_heads * head_dim >= ((int64_t)1 << 31)) return RSWA_ERR_CAPACITY;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RSWA_ERR_ALIGN;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RSWA_ERR_ALIGN;
   if (!isfinite(scale)) return RSWA_ERR_SHAPE;
   if (seq_len == 0) return RSWA_OK;
   MaskedParams p{};
@@ -227,6 +228,7 @@ rswa_status_t rswa_masked_attn(const void *q, const void *k, const void *v, void
   p.k = k;
   p.v = v;
   p.out = out;
+  p.lse = lse;
   p.seq_len = seq_len;
   p.ref_len = ref_len;
   p.window = window;
@@ -235,6 +237,61 @@ rswa_status_t rswa_masked_attn(const void *q, const void *k, const void *v, void
   const float sc = scale == 0.f ? 1.f / sqrtf((float)head_dim) : scale;
   p.scale_log2 = sc * kLog2e;
   const hipError_t e = launch_masked(p, head_dim, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
+}
+
+size_t rswa_masked_bwd_workspace_size(int32_t seq_len, int32_t num_heads) {
+  if (seq_len < 0 || num_heads < 1) return 0;
+  const size_t n_pad = ((size_t)seq_len + 31) / 32 * 32;
+  return 2 * (size_t)num_heads * n_pad * sizeof(float);
+}
+
+rswa_status_t rswa_masked_attn_bwd(const void *q, const void *k, const void *v, const void *out,
+                                   const void *dout, const float *lse, void *dq, void *dk,
+                                   void *dv, int32_t seq_len, int32_t ref_len, int32_t window,
+                                   int32_t num_heads, int32_t head_dim, int32_t dtype,
+                                   int32_t prefix_mode, float scale, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr ||
+      lse == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+    return RSWA_ERR_NULL;
+  if (seq_len < 0 || ref_len < 0 || ref_len > seq_len || window < 1 || num_heads < 1)
+    return RSWA_ERR_SHAPE;
+  if (dtype != RSWA_BF16 || head_dim != 128) return RSWA_ERR_UNSUPPORTED;
+  if (prefix_mode != RSWA_PREFIX_CAUSAL && prefix_mode != RSWA_PREFIX_FULL)
+    return RSWA_ERR_UNSUPPORTED;
+  if ((int64_t)seq_len * num_heads * head_dim >= ((int64_t)1 << 31)) return RSWA_ERR_CAPACITY;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return RSWA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RSWA_ERR_ALIGN;
+  if (!isfinite(scale)) return RSWA_ERR_SHAPE;
+  if (seq_len == 0) return RSWA_OK;
+  const size_t need = rswa_masked_bwd_workspace_size(seq_len, num_heads);
+  if (workspace == nullptr) return RSWA_ERR_NULL;
+  if (!aligned16(workspace)) return RSWA_ERR_ALIGN;
+  if (workspace_bytes < need) return RSWA_ERR_WORKSPACE;
+  MaskedBwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.seq_len = seq_len;
+  p.n_pad = (seq_len + 31) / 32 * 32;
+  p.d_row = static_cast<float *>(workspace);
+  p.lse2 = p.d_row + (size_t)num_heads * p.n_pad;
+  p.ref_len = ref_len;
+  p.window = window;
+  p.heads = num_heads;
+  p.prefix_mode = prefix_mode;
+  p.scale = scale == 0.f ? 1.f / sqrtf((float)head_dim) : scale;
+  p.scale_log2 = p.scale * kLog2e;
+  const hipError_t e = launch_masked_bwd(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
 }
 

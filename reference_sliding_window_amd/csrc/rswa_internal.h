@@ -79,8 +79,26 @@ struct MaskedParams {
   const void *k;
   const void *v;
   void *out;
+  float *lse;  // nullable [H][N], natural log of each row's softmax normaliser
   int32_t seq_len, ref_len, window, heads, prefix_mode;
   float scale_log2;
+};
+
+struct MaskedBwdParams {
+  const void *q;
+  const void *k;
+  const void *v;
+  const void *out;
+  const void *dout;
+  const float *lse;  // [H][N], natural log
+  void *dq;
+  void *dk;
+  void *dv;
+  float *d_row;  // workspace [H][n_pad]: dO_i . O_i
+  float *lse2;   // workspace [H][n_pad]: lse in base 2
+  int32_t seq_len, n_pad, ref_len, window, heads, prefix_mode;
+  float scale;       // softmax scale
+  float scale_log2;  // softmax scale * log2(e)
 };
 
 // Launchers (enqueue only; return the launch's hipError_t).
@@ -88,6 +106,7 @@ hipError_t launch_cache_init(const InitParams &p, int32_t dtype, int32_t head_di
 hipError_t launch_append(const AppendParams &p, int32_t dtype, int32_t head_dim, hipStream_t s);
 hipError_t launch_decode(const DecodeParams &p, int32_t dtype, int32_t head_dim, hipStream_t s);
 hipError_t launch_masked(const MaskedParams &p, int32_t head_dim, hipStream_t s);
+hipError_t launch_masked_bwd(const MaskedBwdParams &p, hipStream_t s);
 hipError_t launch_clear_word(int32_t *word, hipStream_t s);
 
 }  // namespace rswa

@@ -314,6 +314,8 @@ __global__ __launch_bounds__(256, 2) void masked_attn_kernel(MaskedParams p) {
   l += __shfl_xor(l, 32, 64);
   if (!q_ok) return;
   const float inv = 1.f / l;
+  if (p.lse != nullptr && hi == 0)  // natural log of sum_j 2^(c s_j) = (c m + log2 l) ln 2
+    p.lse[(int64_t)h * N + qi] = (m * c + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
   uint16_t *orow = Og + (int64_t)qi * row_stride;
 #pragma unroll
   for (int db = 0; db < kD / 32; ++db) {

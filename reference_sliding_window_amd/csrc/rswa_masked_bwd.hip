@@ -1,0 +1,437 @@
+// Backward of the packed (teacher-forced) R-SWA forward on gfx950 matrix cores.
+//
+// For the loss sum(dO * O) of the forward O_i = softmax(scale K_J q_i) V_J over
+// the two-segment visible set J(i) (WeThinkIn "Unlimited OCR Works：一篇读懂
+// R-SWA…", section 方法展开.3, Eqs. (1)-(4)), with P_ij the softmax weights:
+//   dV_j = sum_i P_ij dO_i,   dP_ij = dO_i . v_j,   D_i = dO_i . O_i,
+//   dS_ij = P_ij (dP_ij - D_i),   dQ_i = scale sum_j dS_ij k_j,
+//   dK_j = scale sum_i dS_ij q_i.
+// P is recomputed from the forward's per-row log-sum-exp. Three kernels:
+//  * bwd_pre_kernel: D_i and the log-sum-exp in base 2 per (head, row);
+//  * bwd_dq_kernel: one workgroup per 128 query rows x head, the forward's
+//    block walk; per 32-key tile S^T = K Q^T and dP^T = V dO^T on matrix cores
+//    (K and V row fragments from LDS, Q and dO rows resident), dS^T in
+//    registers, dQ^T += K^T dS^T with K^T from transposing LDS reads;
+//  * bwd_dkdv_kernel: one workgroup per 128 keys x head, 4 waves x 32 keys with
+//    their K and V rows resident; it walks the 32-row query blocks that see any
+//    of its keys: S = Q K^T and dP = dO V^T (Q, dO row fragments from LDS),
+//    dV += P^T dO and dK += dS^T Q with dO and Q from transposing LDS reads.
+// Q/dO and K/V tiles reach LDS by DMA (global_load_lds_dwordx4), double
+// buffered, into 256-byte rows with swizzled 16-byte chunks (rswa_tile.h).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "rswa_internal.h"
+#include "rswa_tile.h"
+
+namespace rswa {
+namespace {
+
+using namespace tile;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- pre-pass
+// D[h][i] = sum_d dO[i][h][d] O[i][h][d]; lse2[h][i] = lse[h][i] log2(e).
+// Rows past N in each head's padded stretch get D = 0, lse2 = 0.
+// 4 waves x 4 rows per block; 16 lanes per row, 16 bytes each.
+__global__ __launch_bounds__(256) void bwd_pre_kernel(MaskedBwdParams p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 16 + wave * 4 + (lane >> 4);  // = h * Np + i
+  const int c = lane & 15;
+  const int Np = p.n_pad;
+  if (row >= (int64_t)p.heads * Np) return;
+  const int h = (int)(row / Np), i = (int)(row % Np);
+  float acc = 0.f;
+  if (i < p.seq_len) {
+    const int64_t off = ((int64_t)i * p.heads + h) * kD + c * 8;
+    const u32x4_t g = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(p.dout) + off);
+    const u32x4_t o = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(p.out) + off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(__uint_as_float(g[e] << 16), __uint_as_float(o[e] << 16), acc);
+      acc = fmaf(__uint_as_float(g[e] & 0xffff0000u), __uint_as_float(o[e] & 0xffff0000u), acc);
+    }
+  }
+  acc += __shfl_xor(acc, 1, 64);
+  acc += __shfl_xor(acc, 2, 64);
+  acc += __shfl_xor(acc, 4, 64);
+  acc += __shfl_xor(acc, 8, 64);
+  if (c == 0) {
+    p.d_row[row] = acc;
+    p.lse2[row] = i < p.seq_len ? p.lse[(int64_t)h * p.seq_len + i] * kLog2e : 0.f;
+  }
+}
+
+// --------------------------------------------------------------- dQ kernel
+constexpr int kBMq = 128;  // query rows per workgroup
+constexpr int kBNq = 64;   // keys per block (two 32-key tiles)
+
+struct KBlock {
+  int kb0, kend;
+};
+
+// Sets to -inf the scores of keys hidden from query qi (S^T layout: element r
+// of a 32-key tile is key kt0 + 8 (r/4) + 4 hi + r%4 for this lane's query).
+template <bool kWindow>
+__device__ __forceinline__ void mask_st(f32x16_t &s, int kt0, int kend, int qi, int n,
+                                        bool sees_prefix, int hi) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int j = kt0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+    const bool vis = kWindow ? (j < kend && j <= qi && qi - j < n)
+                             : (j < kend && (sees_prefix || j <= qi));
+    s[r] = vis ? s[r] : kNegInf;
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(MaskedBwdParams p) {
+  __shared__ uint16_t k_t0[kBNq * kD], k_t1[kBNq * kD], v_t0[kBNq * kD], v_t1[kBNq * kD];
+  const int N = p.seq_len, H = p.heads, Lm = p.ref_len, n = p.window;
+  const bool full_prefix = p.prefix_mode == RSWA_PREFIX_FULL;
+  const int nqb = (N + kBMq - 1) / kBMq;
+  const int G = nqb * H;
+  int w = blockIdx.x;
+  if ((G & 7) == 0) w = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int h = w / nqb;
+  const int q0 = (w % nqb) * kBMq;
+  const int q_end = min(N, q0 + kBMq);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hi = lane >> 5, l32 = lane & 31;
+  const uint32_t stride = (uint32_t)H * kD;
+  const uint16_t *Qg = static_cast<const uint16_t *>(p.q) + (int64_t)h * kD;
+  const uint16_t *Kg = static_cast<const uint16_t *>(p.k) + (int64_t)h * kD;
+  const uint16_t *Vg = static_cast<const uint16_t *>(p.v) + (int64_t)h * kD;
+  const uint16_t *Gg = static_cast<const uint16_t *>(p.dout) + (int64_t)h * kD;
+
+  const int pre_hi = (full_prefix && q0 < Lm) ? Lm : min(Lm, q_end);
+  const int win_lo = max(Lm, max(q0, Lm) - n + 1);
+  const int win_hi = q_end > Lm ? q_end : win_lo;
+  const int nb_pre = (pre_hi + kBNq - 1) / kBNq;
+  const int nblocks = nb_pre + (win_hi - win_lo + kBNq - 1) / kBNq;
+  auto block_of = [&](int bi) __attribute__((always_inline)) -> KBlock {
+    if (bi < nb_pre) return {bi * kBNq, pre_hi};
+    return {win_lo + (bi - nb_pre) * kBNq, win_hi};
+  };
+
+  const int qw0 = q0 + wave * 32;
+  const int qi = qw0 + l32;
+  const bool q_ok = qi < N;
+  const bool sees_prefix = qi >= Lm || full_prefix;
+  bf16x8_t qf[kD / 16], gf[kD / 16];
+  {
+    const int64_t r = (int64_t)(q_ok ? qi : 0) * stride;
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) {
+      const u32x4_t zero = {0, 0, 0, 0};
+      qf[ks] = as_bf16x8(q_ok ? *reinterpret_cast<const u32x4_t *>(Qg + r + ks * 16 + hi * 8) : zero);
+      gf[ks] = as_bf16x8(q_ok ? *reinterpret_cast<const u32x4_t *>(Gg + r + ks * 16 + hi * 8) : zero);
+    }
+  }
+  const int64_t rq = (int64_t)h * p.n_pad + (q_ok ? qi : 0);
+  const float lse2 = p.lse2[rq];
+  const float Dq = p.d_row[rq];
+  const float c = p.scale_log2;
+
+  f32x16_t dq[kD / 32];
+#pragma unroll
+  for (int j = 0; j < kD / 32; ++j) dq[j] = f32x16_t{};
+
+  uint32_t koff[kD / 16], toff[kD / 32][2];
+#pragma unroll
+  for (int ks = 0; ks < kD / 16; ++ks) koff[ks] = row_frag_off(l32, hi, ks);
+#pragma unroll
+  for (int db = 0; db < kD / 32; ++db) {
+    toff[db][0] = tr_off(lane, db, 0);
+    toff[db][1] = tr_off(lane, db, 1);
+  }
+
+  // DMA of one 64-key block: wave w fills rows 16 w .. 16 w + 15 of both tiles.
+  auto dma_block = [&](const KBlock &bk, uint16_t *kt, uint16_t *vt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row0 = 16 * wave + 4 * j;
+      const int r = min(bk.kb0 + row0 + (lane >> 4), bk.kend - 1);
+      const uint32_t off = __umul24((uint32_t)r, stride);
+      dma_rows(Kg + off, lane, row0, kt);
+      dma_rows(Vg + off, lane, row0, vt);
+    }
+  };
+
+  auto body = [&](int bi, auto mode, auto parity) __attribute__((always_inline)) {
+    constexpr int kMode = decltype(mode)::value;
+    constexpr int P = decltype(parity)::value;
+    const KBlock bk = block_of(bi);
+    const char *kb = reinterpret_cast<const char *>(P ? k_t1 : k_t0);
+    const char *vb = reinterpret_cast<const char *>(P ? v_t1 : v_t0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA of block bi landed
+    __syncthreads();
+    if (bi + 1 < nblocks) dma_block(block_of(bi + 1), P ? k_t0 : k_t1, P ? v_t0 : v_t1);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x16_t s, dp;
+#pragma unroll
+      for (int ks = 0; ks < kD / 16; ++ks) {
+        const bf16x8_t ka = as_bf16x8(*reinterpret_cast<const u32x4_t *>(kb + koff[ks] + kt * 32 * kRowBytes));
+        const bf16x8_t va = as_bf16x8(*reinterpret_cast<const u32x4_t *>(vb + koff[ks] + kt * 32 * kRowBytes));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? f32x16_t{} : s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], ks == 0 ? f32x16_t{} : dp, 0, 0, 0);
+      }
+      if constexpr (kMode == 1) mask_st<false>(s, bk.kb0 + 32 * kt, bk.kend, qi, n, sees_prefix, hi);
+      if constexpr (kMode == 2) mask_st<true>(s, bk.kb0 + 32 * kt, bk.kend, qi, n, sees_prefix, hi);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r0 = 8 * half + 2 * e;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r0], c, -lse2));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r0 + 1], c, -lse2));
+          w4[e] = pack_bf16(p0 * (dp[r0] - Dq), p1 * (dp[r0 + 1] - Dq));
+        }
+        const bf16x8_t dsb = as_bf16x8(u32x4_t{w4[0], w4[1], w4[2], w4[3]});
+        const int st = 2 * kt + half;
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db)
+          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(kb, toff[db][0], toff[db][1], st),
+                                                           dsb, dq[db], 0, 0, 0);
+      }
+    }
+  };
+  auto step = [&](int bi, auto mode) __attribute__((always_inline)) {
+    if (bi & 1)
+      body(bi, mode, std::integral_constant<int, 1>{});
+    else
+      body(bi, mode, std::integral_constant<int, 0>{});
+  };
+
+  if (nblocks > 0) dma_block(block_of(0), k_t0, v_t0);
+  int nb_clear = pre_hi / kBNq;
+  if (!full_prefix && qw0 < Lm) nb_clear = min(nb_clear, (qw0 + 1) / kBNq);
+  __builtin_amdgcn_s_waitcnt(0);
+  int bi = 0;
+  for (; bi < nb_clear; ++bi) step(bi, std::integral_constant<int, 0>{});
+  for (; bi < nb_pre; ++bi) step(bi, std::integral_constant<int, 1>{});
+  for (; bi < nblocks; ++bi) step(bi, std::integral_constant<int, 2>{});
+
+  if (!q_ok) return;
+  // dQ^T accumulator element r of dq[db] is d = 32 db + 8 (r/4) + 4 hi + r%4.
+  uint16_t *orow = static_cast<uint16_t *>(p.dq) + (int64_t)qi * stride + (int64_t)h * kD;
+  const float sc = p.scale;
+#pragma unroll
+  for (int db = 0; db < kD / 32; ++db) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = 32 * db + 8 * g4 + 4 * hi;
+      const u32x2_t w2 = {pack_bf16(dq[db][4 * g4 + 0] * sc, dq[db][4 * g4 + 1] * sc),
+                          pack_bf16(dq[db][4 * g4 + 2] * sc, dq[db][4 * g4 + 3] * sc)};
+      *reinterpret_cast<u32x2_t *>(orow + d0) = w2;
+    }
+  }
+}
+
+// ------------------------------------------------------------- dK/dV kernel
+constexpr int kBK = 128;  // keys per workgroup (4 waves x 32)
+constexpr int kBQ = 32;   // query rows per block
+
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
+  __shared__ uint16_t q_t0[kBQ * kD], q_t1[kBQ * kD], g_t0[kBQ * kD], g_t1[kBQ * kD];
+  const int N = p.seq_len, H = p.heads, Lm = p.ref_len, n = p.window;
+  const bool full_prefix = p.prefix_mode == RSWA_PREFIX_FULL;
+  const int nkb = (N + kBK - 1) / kBK;
+  const int G = nkb * H;
+  int w = blockIdx.x;
+  if ((G & 7) == 0) w = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int h = w / nkb;
+  const int kw0 = (w % nkb) * kBK;
+  const int kmax = min(N, kw0 + kBK) - 1;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hi = lane >> 5, l32 = lane & 31;
+  const uint32_t stride = (uint32_t)H * kD;
+  const uint16_t *Qg = static_cast<const uint16_t *>(p.q) + (int64_t)h * kD;
+  const uint16_t *Kg = static_cast<const uint16_t *>(p.k) + (int64_t)h * kD;
+  const uint16_t *Vg = static_cast<const uint16_t *>(p.v) + (int64_t)h * kD;
+  const uint16_t *Gg = static_cast<const uint16_t *>(p.dout) + (int64_t)h * kD;
+
+  // This lane's key (B operand column / accumulator column of S and dP).
+  const int kj = kw0 + 32 * wave + l32;
+  const bool k_ok = kj < N;
+  bf16x8_t kf[kD / 16], vf[kD / 16];
+  {
+    const int64_t r = (int64_t)(k_ok ? kj : 0) * stride;
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) {
+      const u32x4_t zero = {0, 0, 0, 0};
+      kf[ks] = as_bf16x8(k_ok ? *reinterpret_cast<const u32x4_t *>(Kg + r + ks * 16 + hi * 8) : zero);
+      vf[ks] = as_bf16x8(k_ok ? *reinterpret_cast<const u32x4_t *>(Vg + r + ks * 16 + hi * 8) : zero);
+    }
+  }
+  const bool key_is_prefix = kj < Lm;
+
+  // Query rows that see some key of this workgroup.
+  int q_lo, q_hi;
+  if (kw0 < Lm) {
+    q_lo = full_prefix ? 0 : kw0;
+    q_hi = N;
+  } else {
+    q_lo = kw0;
+    q_hi = min(N, kmax + n);
+  }
+  const int b_lo = q_lo / kBQ;
+  const int nblocks = (q_hi + kBQ - 1) / kBQ - b_lo;
+  // Blocks that hide no (query, key) pair: all keys in the prefix, all rows
+  // output rows, block whole.
+  const bool all_prefix_keys = kmax < Lm;
+
+  f32x16_t dk[kD / 32], dv[kD / 32];
+#pragma unroll
+  for (int j = 0; j < kD / 32; ++j) {
+    dk[j] = f32x16_t{};
+    dv[j] = f32x16_t{};
+  }
+  uint32_t roff[kD / 16], toff[kD / 32][2];
+#pragma unroll
+  for (int ks = 0; ks < kD / 16; ++ks) roff[ks] = row_frag_off(l32, hi, ks);
+#pragma unroll
+  for (int db = 0; db < kD / 32; ++db) {
+    toff[db][0] = tr_off(lane, db, 0);
+    toff[db][1] = tr_off(lane, db, 1);
+  }
+  const float c = p.scale_log2;
+  const float *lse2_h = p.lse2 + (int64_t)h * p.n_pad;
+  const float *d_h = p.d_row + (int64_t)h * p.n_pad;
+
+  // DMA of one 32-row query block: wave w fills rows 8 w .. 8 w + 7 of both tiles.
+  auto dma_block = [&](int qb0, uint16_t *qt, uint16_t *gt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row0 = 8 * wave + 4 * j;
+      const int r = min(qb0 + row0 + (lane >> 4), N - 1);
+      const uint32_t off = __umul24((uint32_t)r, stride);
+      dma_rows(Qg + off, lane, row0, qt);
+      dma_rows(Gg + off, lane, row0, gt);
+    }
+  };
+
+  auto body = [&](int bi, auto masked, auto parity) __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked)::value;
+    constexpr int P = decltype(parity)::value;
+    const int qb0 = (b_lo + bi) * kBQ;
+    const char *qb = reinterpret_cast<const char *>(P ? q_t1 : q_t0);
+    const char *gb = reinterpret_cast<const char *>(P ? g_t1 : g_t0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA of block bi landed
+    __syncthreads();
+    if (bi + 1 < nblocks) dma_block(qb0 + kBQ, P ? q_t0 : q_t1, P ? g_t0 : g_t1);
+    // S = Q K^T and dP = dO V^T: element r is query qb0 + 8 (r/4) + 4 hi + r%4, key kj.
+    f32x16_t s, dp;
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) {
+      const bf16x8_t qa = as_bf16x8(*reinterpret_cast<const u32x4_t *>(qb + roff[ks]));
+      const bf16x8_t ga = as_bf16x8(*reinterpret_cast<const u32x4_t *>(gb + roff[ks]));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], ks == 0 ? f32x16_t{} : s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], ks == 0 ? f32x16_t{} : dp, 0, 0, 0);
+    }
+    // P and dS for this lane's key and 16 queries, in 4 groups of 4 consecutive rows.
+    uint32_t pw[8], dw[8];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int i0 = qb0 + 8 * g + 4 * hi;
+      const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(lse2_h + i0);
+      const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(d_h + i0);
+      float pv[4], dsv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        float x = s[r];
+        if constexpr (kMasked) {
+          const int i = i0 + e;
+          bool vis = i < N && k_ok && kj <= i;
+          if (key_is_prefix) {
+            vis = vis || (i < N && k_ok && full_prefix && i < Lm);  // full prefix: rows < L_m see the prefix
+          } else {
+            vis = vis && i - kj < n;
+          }
+          x = vis ? x : kNegInf;
+        }
+        pv[e] = __builtin_amdgcn_exp2f(fmaf(x, c, -l4[e]));
+        dsv[e] = pv[e] * (dp[r] - d4[e]);
+      }
+      pw[2 * g] = pack_bf16(pv[0], pv[1]);
+      pw[2 * g + 1] = pack_bf16(pv[2], pv[3]);
+      dw[2 * g] = pack_bf16(dsv[0], dsv[1]);
+      dw[2 * g + 1] = pack_bf16(dsv[2], dsv[3]);
+    }
+    // dV += P^T dO and dK += dS^T Q over two 16-query steps; step st uses
+    // elements 8 st .. 8 st + 7 (queries 16 st + {4 hi.., 8 + 4 hi..}).
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const bf16x8_t pa = as_bf16x8(u32x4_t{pw[4 * st], pw[4 * st + 1], pw[4 * st + 2], pw[4 * st + 3]});
+      const bf16x8_t da = as_bf16x8(u32x4_t{dw[4 * st], dw[4 * st + 1], dw[4 * st + 2], dw[4 * st + 3]});
+#pragma unroll
+      for (int db = 0; db < kD / 32; ++db) {
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, tr_operand(gb, toff[db][0], toff[db][1], st),
+                                                         dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, tr_operand(qb, toff[db][0], toff[db][1], st),
+                                                         dk[db], 0, 0, 0);
+      }
+    }
+  };
+  auto step = [&](int bi, auto masked) __attribute__((always_inline)) {
+    if (bi & 1)
+      body(bi, masked, std::integral_constant<int, 1>{});
+    else
+      body(bi, masked, std::integral_constant<int, 0>{});
+  };
+
+  if (nblocks > 0) dma_block(b_lo * kBQ, q_t0, g_t0);
+  __builtin_amdgcn_s_waitcnt(0);
+  // Unmasked run: blocks inside [L_m, N), whole, when every key is a prefix key.
+  int clear_lo = nblocks, clear_hi = nblocks;
+  if (all_prefix_keys) {
+    clear_lo = max(0, (Lm + kBQ - 1) / kBQ - b_lo);
+    clear_hi = max(clear_lo, N / kBQ - b_lo);
+  }
+  int bi = 0;
+  for (; bi < clear_lo; ++bi) step(bi, std::true_type{});
+  for (; bi < clear_hi; ++bi) step(bi, std::false_type{});
+  for (; bi < nblocks; ++bi) step(bi, std::true_type{});
+
+  // Accumulator element r of dk[db] is key kw0 + 32 wave + 8 (r/4) + 4 hi + r%4
+  // and d = 32 db + l32: every lane stores, whatever its own score column.
+  const float sc = p.scale;
+  uint16_t *dkg = static_cast<uint16_t *>(p.dk) + (int64_t)h * kD;
+  uint16_t *dvg = static_cast<uint16_t *>(p.dv) + (int64_t)h * kD;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = kw0 + 32 * wave + 8 * (r >> 2) + 4 * hi + (r & 3);
+    if (key >= N) continue;
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db) {
+      const uint32_t kp = pack_bf16(dk[db][r] * sc, dv[db][r]);
+      dkg[(int64_t)key * stride + 32 * db + l32] = static_cast<uint16_t>(kp & 0xffffu);
+      dvg[(int64_t)key * stride + 32 * db + l32] = static_cast<uint16_t>(kp >> 16);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_masked_bwd(const MaskedBwdParams &p, hipStream_t s) {
+  const int64_t rows = (int64_t)p.heads * p.n_pad;
+  hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t gq = (int64_t)((p.seq_len + kBMq - 1) / kBMq) * p.heads;
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)gq), dim3(256), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t gk = (int64_t)((p.seq_len + kBK - 1) / kBK) * p.heads;
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)gk), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace rswa

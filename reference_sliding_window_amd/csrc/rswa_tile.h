@@ -1,0 +1,81 @@
+// Tile helpers shared by the packed (matrix-core) kernels of librswa. Internal.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rswa {
+namespace tile {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+// Native vectors for 16- and 8-byte moves (HIP's uint4 is a struct whose copies
+// go through private memory).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kD = 128;                   // head dim of the packed kernels
+constexpr int kRowBytes = kD * 2;         // 256-byte bf16 rows in LDS, no padding
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ constexpr bf16x2_t kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const f32x2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// Physical 16-byte chunk of logical chunk c in row r of a 256-byte-row LDS tile:
+// c ^ chunk_swz(r). Eight consecutive rows read at one chunk (MFMA row fragments)
+// and four consecutive rows read at four neighbouring chunks (transposing reads)
+// then hit distinct banks.
+__device__ __forceinline__ int chunk_swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+
+// Byte offset of the row fragment lane (l32, hi) reads for k-step ks: row l32,
+// logical chunk 2 ks + hi (8 consecutive d starting at 16 ks + 8 hi).
+__device__ __forceinline__ uint32_t row_frag_off(int l32, int hi, int ks) {
+  return l32 * kRowBytes + 16 * ((2 * ks + hi) ^ chunk_swz(l32));
+}
+
+// Byte offset for the transposing read (ds_read_b64_tr_b16) that builds half h2
+// of a 32x32x16 MFMA operand holding 8 tile rows x one d per lane: within each
+// 16-lane group G = lane / 16, lane s addresses row 8 h2 + 4 (G / 2) + e and
+// d = 32 db + 16 (G % 2) + 4 q (e = s / 4 mod 4, q = s mod 4); lane i of the
+// group then receives d = 32 db + lane % 32 of the rows base + e, e = 0..3. The
+// row-dependent part of the swizzle is the same for every 16-row step st, so
+// step st adds 16 st rows.
+__device__ __forceinline__ uint32_t tr_off(int lane, int db, int h2) {
+  const int G = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+  const int row = 8 * h2 + 4 * (G >> 1) + e;
+  const int chunk = (4 * db + 2 * (G & 1) + (q >> 1)) ^ chunk_swz(row);
+  return row * kRowBytes + 16 * chunk + 8 * (q & 1);
+}
+
+// The 32x32x16 operand for 16-row step st and d block db from two transposing reads.
+__device__ __forceinline__ bf16x8_t tr_operand(const char *tile, uint32_t off0, uint32_t off1, int st) {
+  const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(tile + off0 + 16 * st * kRowBytes));
+  const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(tile + off1 + 16 * st * kRowBytes));
+  const u32x2_t a0 = __builtin_bit_cast(u32x2_t, v0), a1 = __builtin_bit_cast(u32x2_t, v1);
+  return as_bf16x8(u32x4_t{a0.x, a0.y, a1.x, a1.y});
+}
+
+// One DMA instruction (global_load_lds_dwordx4): 64 lanes x 16 bytes land at
+// tile + row0 * 256 + 16 lane, i.e. rows row0 .. row0 + 3, physical chunk
+// lane % 16. Lane L loads global row `grow` (already clamped by the caller), logical
+// chunk (L % 16) ^ chunk_swz(row0 + L / 16).
+__device__ __forceinline__ void dma_rows(const uint16_t *src_row, int lane, int row0, uint16_t *tile) {
+  const int r = row0 + (lane >> 4);
+  const int c = (lane & 15) ^ chunk_swz(r);
+  char *dst = reinterpret_cast<char *>(tile) + row0 * kRowBytes;
+  __builtin_amdgcn_global_load_lds(src_row + 8 * c, (lds_void_t *)dst, 16, 0, 0);
+}
+
+}  // namespace tile
+}  // namespace rswa

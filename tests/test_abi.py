@@ -128,7 +128,44 @@ def test_masked_argument_checks():
     assert m(prefix_mode=3) == rs.RSWA_ERR_UNSUPPORTED
     assert m(k=A + 2) == rs.RSWA_ERR_ALIGN
     assert m(scale=math.nan) == rs.RSWA_ERR_SHAPE
+    assert m(lse=A + 2) == rs.RSWA_ERR_ALIGN
+    assert m(seq_len=2 ** 20, ref_len=0, num_heads=16) == rs.RSWA_ERR_CAPACITY
     assert m(seq_len=0, ref_len=0) == rs.RSWA_OK   # nothing to do, nothing enqueued
+
+
+def test_masked_bwd_workspace_size():
+    assert rs.rswa_masked_bwd_workspace_size(-1, 2) == 0
+    assert rs.rswa_masked_bwd_workspace_size(10, 0) == 0
+    assert rs.rswa_masked_bwd_workspace_size(0, 2) == 0
+    # two float arrays [H][roundup(N, 32)]
+    assert rs.rswa_masked_bwd_workspace_size(1, 2) == 2 * 2 * 32 * 4
+    assert rs.rswa_masked_bwd_workspace_size(32768, 16) == 2 * 16 * 32768 * 4
+    assert rs.rswa_masked_bwd_workspace_size(300, 3) == 2 * 3 * 320 * 4
+
+
+def test_masked_bwd_argument_checks():
+    ws = rs.rswa_masked_bwd_workspace_size(300, 2)
+    base = dict(q=A, k=A, v=A, out=A, dout=A, lse=A, dq=A, dk=A, dv=A, seq_len=300, ref_len=40,
+                window=8, num_heads=2, head_dim=128, workspace=A, workspace_bytes=ws)
+    b = lambda **kw: rs.rswa_masked_attn_bwd(**{**base, **kw}, check=False)
+    for name in ("q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv"):
+        assert b(**{name: None}) == rs.RSWA_ERR_NULL, name
+    for name in ("q", "k", "v", "out", "dout", "dq", "dk", "dv"):
+        assert b(**{name: A + 8}) == rs.RSWA_ERR_ALIGN, name
+    assert b(lse=A + 2) == rs.RSWA_ERR_ALIGN
+    assert b(ref_len=301) == rs.RSWA_ERR_SHAPE
+    assert b(seq_len=-1) == rs.RSWA_ERR_SHAPE
+    assert b(window=0) == rs.RSWA_ERR_SHAPE
+    assert b(num_heads=0) == rs.RSWA_ERR_SHAPE
+    assert b(head_dim=64) == rs.RSWA_ERR_UNSUPPORTED
+    assert b(dtype=rs.RSWA_FP32) == rs.RSWA_ERR_UNSUPPORTED
+    assert b(prefix_mode=2) == rs.RSWA_ERR_UNSUPPORTED
+    assert b(scale=math.inf) == rs.RSWA_ERR_SHAPE
+    assert b(seq_len=2 ** 20, ref_len=0, num_heads=16) == rs.RSWA_ERR_CAPACITY
+    assert b(workspace=None, workspace_bytes=0) == rs.RSWA_ERR_NULL
+    assert b(workspace_bytes=ws - 1) == rs.RSWA_ERR_WORKSPACE
+    assert b(workspace=A + 4) == rs.RSWA_ERR_ALIGN
+    assert b(seq_len=0, ref_len=0, workspace=None, workspace_bytes=0) == rs.RSWA_OK
 
 
 def test_check_device_error_null_arguments():

@@ -1,0 +1,221 @@
+"""GPU parity of the packed forward's log-sum-exp output and of the packed
+backward (rswa_masked_attn_bwd) against the oracle, through the C ABI.
+
+Gradient tolerance: the gradients are bf16 outputs whose size grows with the
+number of terms summed (a prefix key's dK/dV gathers every row that sees it),
+and the kernels round P and dS to bf16 as matrix-core operands, so the error is
+relative to the gradient's magnitude: max|diff| <= 2e-2 * max(1, max|ref|) and
+||diff||_2 / ||ref||_2 <= 1e-2. The log-sum-exp is fp32, but the forward sums
+the probabilities it has rounded to bf16 (each within 2^-9 relative), so its
+normaliser is within a factor 1 +- 2^-9 of the exact one:
+|diff| <= 2^-9 + 2e-4 + 1e-5 |ref| (the rest covers fp32 scores and exp2)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.rswa as orc
+import reference_sliding_window_amd as rs
+import workloads as wl
+from gpu_util import check_close, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+CAUSAL, FULL = rs.RSWA_PREFIX_CAUSAL, rs.RSWA_PREFIX_FULL
+
+
+def banner(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def check_grad(got, ref, what):
+    d = got - ref
+    scale = max(1.0, float(np.abs(ref).max()) if ref.size else 1.0)
+    maxabs = float(np.abs(d).max()) if d.size else 0.0
+    rel = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300))
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    if np.linalg.norm(ref) == 0.0:  # e.g. one visible key: dS = 0 exactly
+        rel = 0.0
+    assert maxabs <= 2e-2 * scale and rel <= 1e-2, \
+        f"{what}: max|d|={maxabs:.3e} (<= {2e-2 * scale:.3e}) rel={rel:.3e} (<= 1e-2)"
+    return maxabs, rel
+
+
+class PackedRun:
+    """Forward (with lse) and backward of one packed sequence on the device."""
+
+    def __init__(self, N, L_m, n, H, mode, seed, sigma=1.0):
+        self.mw = wl.MaskedWorkload("masked-bwd", seq_len=N, heads=H, head_dim=128, ref_len=L_m,
+                                    window=n, dtype="bf16", sigma=sigma, base_seed=seed)
+        self.N, self.L_m, self.n, self.H, self.mode = N, L_m, n, H, mode
+        self.Q, self.K, self.V = wl.packed_qkv(self.mw)
+        self.G = wl.packed_dout(self.mw)
+        self.Qd, self.Kd, self.Vd, self.Gd = (to_dev(x, "bf16") for x in (self.Q, self.K, self.V, self.G))
+        shape = (N, H, 128)
+        self.out = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty((H, N), dtype=torch.float32, device="cuda")
+        self.dq = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        self.dk = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        self.dv = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        nbytes = rs.rswa_masked_bwd_workspace_size(N, H)
+        self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+
+    def forward(self):
+        rs.rswa_masked_attn(self.Qd, self.Kd, self.Vd, self.out, self.N, self.L_m, self.n, self.H, 128,
+                            rs.RSWA_BF16, self.mode, 0.0, lse=self.lse)
+
+    def backward(self):
+        rs.rswa_masked_attn_bwd(self.Qd, self.Kd, self.Vd, self.out, self.Gd, self.lse, self.dq, self.dk,
+                                self.dv, self.N, self.L_m, self.n, self.H, 128, rs.RSWA_BF16, self.mode,
+                                0.0, self.ws)
+
+    def f64(self):
+        f = lambda a: wl.to_f64(a, "bf16")
+        return f(self.Q), f(self.K), f(self.V), f(self.G)
+
+
+SMALL_CASES = [
+    (300, 40, 8, CAUSAL),
+    (300, 40, 8, FULL),
+    (1, 1, 128, CAUSAL),
+    (1, 0, 1, CAUSAL),
+    (257, 0, 16, CAUSAL),
+    (200, 200, 4, FULL),
+    (200, 200, 4, CAUSAL),
+    (513, 130, 128, CAUSAL),
+    (640, 97, 1, CAUSAL),
+    (700, 300, 200, FULL),
+    (161, 33, 1000, CAUSAL),
+]
+
+
+@pytest.mark.parametrize("N,L_m,n,mode", SMALL_CASES[:4] + SMALL_CASES[7:8])
+def test_forward_lse_every_row(N, L_m, n, mode):
+    banner(f"packed lse N={N} L_m={L_m} n={n} mode={mode}")
+    r = PackedRun(N, L_m, n, 2, mode, seed=5000 + N + L_m + n + mode)
+    r.forward()
+    torch.cuda.synchronize()
+    Q, K, _, _ = r.f64()
+    ref = orc.masked_logsumexp_rows(Q, K, range(N), L_m, n, r.mw.scale, mode)  # [N][H]
+    got = r.lse.cpu().numpy().astype(np.float64).T
+    err = np.abs(got - ref)
+    assert np.isfinite(got).all()
+    assert (err <= 2.0 ** -9 + 2e-4 + 1e-5 * np.abs(ref)).all(), f"lse max err {err.max():.3e}"
+
+
+def test_forward_lse_does_not_change_output():
+    banner("packed forward with and without lse")
+    r = PackedRun(513, 130, 128, 2, CAUSAL, seed=77)
+    r.forward()
+    a = r.out.clone()
+    rs.rswa_masked_attn(r.Qd, r.Kd, r.Vd, r.out, r.N, r.L_m, r.n, r.H, 128, rs.RSWA_BF16, CAUSAL, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), r.out.view(torch.int16))
+
+
+@pytest.mark.parametrize("N,L_m,n,mode", SMALL_CASES)
+def test_backward_small_every_row_and_key(N, L_m, n, mode):
+    banner(f"packed bwd N={N} L_m={L_m} n={n} mode={mode}")
+    r = PackedRun(N, L_m, n, 2, mode, seed=6000 + N + L_m + n + mode)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    Q, K, V, G = r.f64()
+    dQ, dK, dV = orc.masked_attention_backward(Q, K, V, G, L_m, n, r.mw.scale, mode)
+    tag = f"N={N} L_m={L_m} n={n} mode={mode}"
+    check_grad(to_f64(r.dq), dQ, f"dQ {tag}")
+    check_grad(to_f64(r.dk), dK, f"dK {tag}")
+    check_grad(to_f64(r.dv), dV, f"dV {tag}")
+
+
+def test_backward_is_deterministic():
+    banner("packed bwd determinism")
+    r = PackedRun(700, 300, 200, 2, FULL, seed=9)
+    r.forward()
+    r.backward()
+    first = [t.clone() for t in (r.dq, r.dk, r.dv)]
+    r.backward()
+    torch.cuda.synchronize()
+    for a, b in zip(first, (r.dq, r.dk, r.dv)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_backward_medium_every_row_and_key():
+    """Long query walks for the prefix keys (~3000 rows each), several heads."""
+    N, L_m, n, H = 4096, 1000, 128, 2
+    banner(f"packed bwd medium N={N} L_m={L_m} n={n} H={H}")
+    r = PackedRun(N, L_m, n, H, CAUSAL, seed=31337)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    Q, K, V, G = r.f64()
+    dQ, dK, dV = orc.masked_attention_backward(Q, K, V, G, L_m, n, r.mw.scale, CAUSAL)
+    for name, got, ref in (("dQ", r.dq, dQ), ("dK", r.dk, dK), ("dV", r.dv, dV)):
+        ma, rel = check_grad(to_f64(got), ref, f"{name} medium")
+        print(f"{name}: max|d|={ma:.3e} rel={rel:.3e}")
+
+
+@pytest.mark.slow
+def test_backward_32k_sampled_and_column_sums():
+    """Full packed 32K size: dQ on sampled rows and dK/dV on sampled output-segment
+    keys exactly (the rows that see such a key are the n rows from it on), and for
+    every key the column sums the softmax fixes: sum_j dV_j = sum_i dO_i (each
+    row's weights sum to one) and sum_j dK_j = 0 (each row's dS sums to zero)."""
+    mw = wl.PACKED_32K
+    N, L_m, n, H = mw.seq_len, mw.ref_len, mw.window, mw.heads
+    banner(f"packed 32K bwd N={N} L_m={L_m} n={n} H={H}")
+    r = PackedRun(N, L_m, n, H, CAUSAL, seed=mw.base_seed, sigma=mw.sigma)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    dq, dk, dv = to_f64(r.dq), to_f64(r.dk), to_f64(r.dv)
+    assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
+    f = lambda a: wl.to_f64(a, "bf16")
+    K, V = f(r.K), f(r.V)
+    rng = np.random.default_rng(12)
+    rows = sorted(set([0, 1, L_m - 1, L_m, L_m + 1, L_m + n - 1, L_m + n, 4095, 4096, N - 1] +
+                      rng.integers(0, N, 24).tolist()))
+    Qr, Gr = _RowView(f(r.Q[rows]), rows), _RowView(f(r.G[rows]), rows)
+    dQ, _, _ = orc.masked_attention_backward(Qr, K, V, Gr, L_m, n, mw.scale, CAUSAL, rows=rows)
+    ma, rel = check_grad(dq[rows], dQ, "dQ 32K sampled rows")
+    print(f"dQ rows: max|d|={ma:.3e} rel={rel:.3e}")
+    # output-segment keys in three runs of 8 (near L_m, mid-sequence, the tail);
+    # heads 0 and H-1 only (a head's gradients depend on that head alone)
+    hs = [0, H - 1]
+    Kh, Vh = K[:, hs], V[:, hs]
+    mid = (L_m + N) // 2
+    for a in (L_m, mid, N - 8):
+        see = list(range(a, min(N, a + 8 + n - 1)))
+        Qs = _RowView(f(r.Q[see])[:, hs], see)
+        Gs = _RowView(f(r.G[see])[:, hs], see)
+        _, dK, dV = orc.masked_attention_backward(Qs, Kh, Vh, Gs, L_m, n, mw.scale, CAUSAL, rows=see)
+        check_grad(dk[a:a + 8][:, hs], dK[a:a + 8], f"dK keys {a}..{a + 7}")
+        check_grad(dv[a:a + 8][:, hs], dV[a:a + 8], f"dV keys {a}..{a + 7}")
+    # column sums over every key, per head and dimension (fp64 sums of the bf16 results)
+    g_sum = f(r.G).sum(axis=0)
+    dv_sum = dv.sum(axis=0)
+    check_grad(dv_sum, g_sum, "sum_j dV_j vs sum_i dO_i")
+    # sum_j dK_j vanishes in exact arithmetic; here each row's dS sums to a
+    # rounding residue (the forward rounds P to bf16 for its normaliser and
+    # output, the backward rounds dS), so bound the sum by 2^-9 of the mass
+    # that cancels: sum_j |dK_j| per head and dimension.
+    dk_sum = dk.sum(axis=0)
+    bound = 2.0 ** -9 * np.abs(dk).sum(axis=0)
+    worst = float((np.abs(dk_sum) / bound).max())
+    print(f"sum_j dK_j: max |sum| = {np.abs(dk_sum).max():.3e}, worst |sum| / bound = {worst:.3f}")
+    assert worst <= 1.0, f"sum_j dK_j exceeds 2^-9 sum_j |dK_j| (ratio {worst:.3f})"
+
+
+class _RowView:
+    """Indexes like the full [N][H][d] array for the given rows only."""
+
+    def __init__(self, rows_arr, rows):
+        self.a = rows_arr
+        self.pos = {r: i for i, r in enumerate(rows)}
+        self.shape = (max(rows) + 1,) + rows_arr.shape[1:]
+
+    def __getitem__(self, i):
+        if isinstance(i, tuple):
+            return self.a[self.pos[int(i[0])]][i[1:]]
+        return self.a[self.pos[int(i)]]

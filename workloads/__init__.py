@@ -30,7 +30,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 # tensor ids used in seed words
-TID_Q, TID_K, TID_V, TID_KREF, TID_VREF, TID_RAGGED = 0, 1, 2, 3, 4, 5
+TID_Q, TID_K, TID_V, TID_KREF, TID_VREF, TID_RAGGED, TID_DOUT = 0, 1, 2, 3, 4, 5, 6
 
 PAGE_TOKENS = 256   # vision tokens per 1024x1024 page
 PROMPT_TOKENS = 32  # prompt length (not stated on the pages; fixed here)
@@ -196,6 +196,12 @@ def packed_qkv(w: MaskedWorkload, threads: int = 3):
     with ThreadPoolExecutor(threads) as ex:
         return tuple(ex.map(lambda tid: draw(w.dtype, w.sigma, shape, w.base_seed, tid),
                             (TID_Q, TID_K, TID_V)))
+
+
+def packed_dout(w: MaskedWorkload, sigma: float = 1.0):
+    """Upstream gradient dO of the packed forward's output, [N][H][d] in storage
+    form, N(0, sigma^2) (the loss is sum(dO * O))."""
+    return draw(w.dtype, sigma, (w.seq_len, w.heads, w.head_dim), w.base_seed, TID_DOUT)
 
 
 # --------------------------------------------------------------------------- ragged
