@@ -185,11 +185,11 @@ RSWA_API rswa_status_t rswa_masked_attn(const void *q, const void *k, const void
                                int32_t prefix_mode, float scale, void *stream);
 
 /*
- * Bytes of device workspace rswa_masked_attn_bwd needs for seq_len rows and
- * num_heads heads (two float arrays [num_heads][roundup(seq_len, 32)]). 0 for
- * invalid sizes.
+ * Bytes of device workspace rswa_masked_attn_bwd needs for these sizes and
+ * num_parts (0 = the library's choice, as in the call). 0 for invalid sizes.
  */
-RSWA_API size_t rswa_masked_bwd_workspace_size(int32_t seq_len, int32_t num_heads);
+RSWA_API size_t rswa_masked_bwd_workspace_size(int32_t seq_len, int32_t ref_len, int32_t num_heads,
+                                               int32_t num_parts);
 
 /*
  * Backward of rswa_masked_attn for the loss sum(dout * out): the gradients of
@@ -205,20 +205,26 @@ RSWA_API size_t rswa_masked_bwd_workspace_size(int32_t seq_len, int32_t num_head
  *  lse          device float [num_heads][seq_len] from rswa_masked_attn.
  *  dq, dk, dv   device [seq_len][num_heads][head_dim] bf16, written whole
  *               (keys no row sees get zero). Must not alias the inputs.
+ *  num_parts    0 = the library's choice; otherwise 1..64: the rows that
+ *               see a reference-segment key are walked in this many runs
+ *               whose fp32 partial sums are added in a fixed order (more
+ *               runs spread long walks over more compute units). The
+ *               result does not depend on it beyond fp32 rounding.
  *  workspace    device, 16-byte aligned, >= rswa_masked_bwd_workspace_size
- *               bytes; its contents on entry do not matter.
+ *               bytes for the same sizes and num_parts; its contents on entry
+ *               do not matter.
  * Same restrictions as the forward (RSWA_BF16, head_dim 128). Matrix products
  * run on bf16 matrix cores with fp32 accumulation; P and dS are rounded to
- * bf16 as operands. Results do not depend on the launch beyond that: the
- * kernels use no atomics.
+ * bf16 as operands. The kernels use no atomics: repeated calls give
+ * identical bits.
  */
 RSWA_API rswa_status_t rswa_masked_attn_bwd(const void *q, const void *k, const void *v,
                                    const void *out, const void *dout, const float *lse,
                                    void *dq, void *dk, void *dv, int32_t seq_len,
                                    int32_t ref_len, int32_t window, int32_t num_heads,
                                    int32_t head_dim, int32_t dtype, int32_t prefix_mode,
-                                   float scale, void *workspace, size_t workspace_bytes,
-                                   void *stream);
+                                   float scale, int32_t num_parts, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 /*
  * Synchronise `stream`, read the cache's device error word into *flags

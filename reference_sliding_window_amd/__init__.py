@@ -88,9 +88,9 @@ def _lib() -> ctypes.CDLL:
             "rswa_decode_workspace_size": (SZ, [D, I32]),
             "rswa_decode_attn": (I32, [D, P, P, P, P, F, I32, P, SZ, P]),
             "rswa_masked_attn": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, P]),
-            "rswa_masked_bwd_workspace_size": (SZ, [I32, I32]),
+            "rswa_masked_bwd_workspace_size": (SZ, [I32, I32, I32, I32]),
             "rswa_masked_attn_bwd": (I32, [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
-                                           I32, F, P, SZ, P]),
+                                           I32, F, I32, P, SZ, P]),
             "rswa_check_device_error": (I32, [D, ctypes.POINTER(I32), P]),
         }
         for name, (res, args) in sig.items():
@@ -177,22 +177,24 @@ def rswa_masked_attn(q, k, v, out, seq_len: int, ref_len: int, window: int, num_
     return _check(st, "rswa_masked_attn") if check else st
 
 
-def rswa_masked_bwd_workspace_size(seq_len: int, num_heads: int) -> int:
-    return _lib().rswa_masked_bwd_workspace_size(seq_len, num_heads)
+def rswa_masked_bwd_workspace_size(seq_len: int, ref_len: int, num_heads: int,
+                                   num_parts: int = 0) -> int:
+    return _lib().rswa_masked_bwd_workspace_size(seq_len, ref_len, num_heads, num_parts)
 
 
 def rswa_masked_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, seq_len: int, ref_len: int,
                          window: int, num_heads: int, head_dim: int, dtype: int = RSWA_BF16,
                          prefix_mode: int = RSWA_PREFIX_CAUSAL, scale: float = 0.0,
-                         workspace=None, workspace_bytes: int | None = None, stream=None,
-                         check=True) -> int:
+                         workspace=None, workspace_bytes: int | None = None, num_parts: int = 0,
+                         stream=None, check=True) -> int:
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
             workspace.numel() * workspace.element_size()
     st = _lib().rswa_masked_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
                                      _ptr(dq), _ptr(dk), _ptr(dv), seq_len, ref_len, window,
                                      num_heads, head_dim, dtype, prefix_mode, float(scale),
-                                     _ptr(workspace), int(workspace_bytes), _stream(stream))
+                                     int(num_parts), _ptr(workspace), int(workspace_bytes),
+                                     _stream(stream))
     return _check(st, "rswa_masked_attn_bwd") if check else st
 
 

@@ -15,6 +15,7 @@ namespace rswa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int32_t kMaxBwdParts = 64;
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
@@ -70,6 +71,24 @@ WorkspaceLayout decode_workspace_layout(int32_t batch, int32_t heads, int32_t he
   w.seq_state = w.part_ml + round_up(units * 2 * sizeof(float), 256);
   w.total = w.seq_state + round_up((size_t)batch * sizeof(int32_t), 256);
   return w;
+}
+
+BwdPlan plan_masked_bwd(int32_t seq_len, int32_t ref_len, int32_t heads, int32_t requested_parts) {
+  BwdPlan b{};
+  b.n_pad = (seq_len + 31) / 32 * 32;
+  b.nkb_pre = (ref_len + 127) / 128;
+  b.nkb_win = (seq_len + 127) / 128 - b.nkb_pre;
+  b.kpre = 128 * b.nkb_pre;
+  // A reference-segment key block walks up to ceil(seq_len / 32) query blocks;
+  // runs of about 256 blocks keep those walks from setting the kernel's length.
+  int32_t parts = requested_parts;
+  if (parts == 0) parts = ((seq_len + 31) / 32 + 255) / 256;
+  if (parts < 1) parts = 1;
+  if (b.nkb_pre == 0) parts = 1;
+  b.parts = parts;
+  b.bytes_rows = 2 * (size_t)heads * b.n_pad * sizeof(float);
+  b.bytes_parts = parts > 1 ? 2 * (size_t)parts * heads * b.kpre * 128 * sizeof(float) : 0;
+  return b;
 }
 
 }  // namespace rswa
@@ -240,18 +259,21 @@ rswa_status_t rswa_masked_attn(const void *q, const void *k, const void *v, void
   return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
 }
 
-size_t rswa_masked_bwd_workspace_size(int32_t seq_len, int32_t num_heads) {
-  if (seq_len < 0 || num_heads < 1) return 0;
-  const size_t n_pad = ((size_t)seq_len + 31) / 32 * 32;
-  return 2 * (size_t)num_heads * n_pad * sizeof(float);
+size_t rswa_masked_bwd_workspace_size(int32_t seq_len, int32_t ref_len, int32_t num_heads,
+                                      int32_t num_parts) {
+  if (seq_len < 0 || ref_len < 0 || ref_len > seq_len || num_heads < 1 || num_parts < 0 ||
+      num_parts > kMaxBwdParts)
+    return 0;
+  const BwdPlan b = plan_masked_bwd(seq_len, ref_len, num_heads, num_parts);
+  return b.bytes_rows + b.bytes_parts;
 }
 
 rswa_status_t rswa_masked_attn_bwd(const void *q, const void *k, const void *v, const void *out,
                                    const void *dout, const float *lse, void *dq, void *dk,
                                    void *dv, int32_t seq_len, int32_t ref_len, int32_t window,
                                    int32_t num_heads, int32_t head_dim, int32_t dtype,
-                                   int32_t prefix_mode, float scale, void *workspace,
-                                   size_t workspace_bytes, void *stream) {
+                                   int32_t prefix_mode, float scale, int32_t num_parts,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr ||
       lse == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
     return RSWA_ERR_NULL;
@@ -266,8 +288,10 @@ rswa_status_t rswa_masked_attn_bwd(const void *q, const void *k, const void *v, 
     return RSWA_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RSWA_ERR_ALIGN;
   if (!isfinite(scale)) return RSWA_ERR_SHAPE;
+  if (num_parts < 0 || num_parts > kMaxBwdParts) return RSWA_ERR_SHAPE;
   if (seq_len == 0) return RSWA_OK;
-  const size_t need = rswa_masked_bwd_workspace_size(seq_len, num_heads);
+  const BwdPlan plan = plan_masked_bwd(seq_len, ref_len, num_heads, num_parts);
+  const size_t need = plan.bytes_rows + plan.bytes_parts;
   if (workspace == nullptr) return RSWA_ERR_NULL;
   if (!aligned16(workspace)) return RSWA_ERR_ALIGN;
   if (workspace_bytes < need) return RSWA_ERR_WORKSPACE;
@@ -282,9 +306,17 @@ rswa_status_t rswa_masked_attn_bwd(const void *q, const void *k, const void *v, 
   p.dk = dk;
   p.dv = dv;
   p.seq_len = seq_len;
-  p.n_pad = (seq_len + 31) / 32 * 32;
+  p.n_pad = plan.n_pad;
   p.d_row = static_cast<float *>(workspace);
   p.lse2 = p.d_row + (size_t)num_heads * p.n_pad;
+  p.parts = plan.parts;
+  p.nkb_pre = plan.nkb_pre;
+  p.nkb_win = plan.nkb_win;
+  p.kpre = plan.kpre;
+  if (plan.parts > 1) {
+    p.part_dk = p.lse2 + (size_t)num_heads * p.n_pad;
+    p.part_dv = p.part_dk + (size_t)plan.parts * num_heads * plan.kpre * 128;
+  }
   p.ref_len = ref_len;
   p.window = window;
   p.heads = num_heads;

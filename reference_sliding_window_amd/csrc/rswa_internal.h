@@ -94,9 +94,15 @@ struct MaskedBwdParams {
   void *dq;
   void *dk;
   void *dv;
-  float *d_row;  // workspace [H][n_pad]: dO_i . O_i
-  float *lse2;   // workspace [H][n_pad]: lse in base 2
+  float *d_row;    // workspace [H][n_pad]: dO_i . O_i
+  float *lse2;     // workspace [H][n_pad]: lse in base 2
+  float *part_dk;  // workspace [parts][H][kpre][d]: partial dK of the segment's key blocks
+  float *part_dv;  // workspace [parts][H][kpre][d]
   int32_t seq_len, n_pad, ref_len, window, heads, prefix_mode;
+  int32_t parts;    // runs each reference-segment key block's query walk is cut into
+  int32_t nkb_pre;  // 128-key blocks starting below ref_len
+  int32_t nkb_win;  // the remaining 128-key blocks
+  int32_t kpre;     // 128 * nkb_pre
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
 };
@@ -106,6 +112,13 @@ hipError_t launch_cache_init(const InitParams &p, int32_t dtype, int32_t head_di
 hipError_t launch_append(const AppendParams &p, int32_t dtype, int32_t head_dim, hipStream_t s);
 hipError_t launch_decode(const DecodeParams &p, int32_t dtype, int32_t head_dim, hipStream_t s);
 hipError_t launch_masked(const MaskedParams &p, int32_t head_dim, hipStream_t s);
+// Work split of the packed backward (host-known sizes only).
+struct BwdPlan {
+  int32_t parts, nkb_pre, nkb_win, n_pad, kpre;
+  size_t bytes_rows;   // d_row + lse2
+  size_t bytes_parts;  // part_dk + part_dv (0 when parts == 1)
+};
+BwdPlan plan_masked_bwd(int32_t seq_len, int32_t ref_len, int32_t heads, int32_t requested_parts);
 hipError_t launch_masked_bwd(const MaskedBwdParams &p, hipStream_t s);
 hipError_t launch_clear_word(int32_t *word, hipStream_t s);
 

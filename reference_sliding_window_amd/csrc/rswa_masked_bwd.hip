@@ -167,8 +167,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(MaskedBwdParams p) {
     const KBlock bk = block_of(bi);
     const char *kb = reinterpret_cast<const char *>(P ? k_t1 : k_t0);
     const char *vb = reinterpret_cast<const char *>(P ? v_t1 : v_t0);
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA of block bi landed
-    __syncthreads();
+    wait_vmcnt<0>();  // this wave's DMA of block bi landed
+    block_barrier();  // every wave's did; the other buffer is no longer read
     if (bi + 1 < nblocks) dma_block(block_of(bi + 1), P ? k_t0 : k_t1, P ? v_t0 : v_t1);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -208,10 +208,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(MaskedBwdParams p) {
       body(bi, mode, std::integral_constant<int, 0>{});
   };
 
+  wait_vmcnt<0>();  // resident Q/dO rows landed (the compiler does not count the DMA)
   if (nblocks > 0) dma_block(block_of(0), k_t0, v_t0);
   int nb_clear = pre_hi / kBNq;
   if (!full_prefix && qw0 < Lm) nb_clear = min(nb_clear, (qw0 + 1) / kBNq);
-  __builtin_amdgcn_s_waitcnt(0);
   int bi = 0;
   for (; bi < nb_clear; ++bi) step(bi, std::integral_constant<int, 0>{});
   for (; bi < nb_pre; ++bi) step(bi, std::integral_constant<int, 1>{});
@@ -234,19 +234,47 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(MaskedBwdParams p) {
 }
 
 // ------------------------------------------------------------- dK/dV kernel
-constexpr int kBK = 128;  // keys per workgroup (4 waves x 32)
-constexpr int kBQ = 32;   // query rows per block
+constexpr int kBK = 128;    // keys per workgroup (4 waves x 32)
+constexpr int kBQ = 32;     // query rows per block
+constexpr int kStages = 4;  // LDS ring of query blocks: one in use, one computed ahead, two in flight
 
+struct DkdvStage {
+  uint16_t q[kBQ * kD];
+  uint16_t g[kBQ * kD];
+  float ld[2 * kBQ];  // the block's rows: lse in base 2, then D
+};
+
+// Work of one workgroup: 128 keys of one head and a run of query blocks.
+// Key blocks that hold reference-segment keys are seen by every later row; their
+// walk is cut into `parts` runs of equal length whose fp32 partial sums a
+// reduction adds up (parts > 1). Tasks are dealt to the 8 XCDs (block index mod
+// 8) so that each (head, part) lands whole on one XCD, its key blocks walking the
+// same Q/dO rows through one L2; the short output-segment tasks follow.
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
-  __shared__ uint16_t q_t0[kBQ * kD], q_t1[kBQ * kD], g_t0[kBQ * kD], g_t1[kBQ * kD];
+  __shared__ DkdvStage sm[kStages];
   const int N = p.seq_len, H = p.heads, Lm = p.ref_len, n = p.window;
   const bool full_prefix = p.prefix_mode == RSWA_PREFIX_FULL;
-  const int nkb = (N + kBK - 1) / kBK;
-  const int G = nkb * H;
-  int w = blockIdx.x;
-  if ((G & 7) == 0) w = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  const int h = w / nkb;
-  const int kw0 = (w % nkb) * kBK;
+  const int S = p.parts, nkb_pre = p.nkb_pre, nkb_win = p.nkb_win;
+  const int x = blockIdx.x & 7, kx = blockIdx.x >> 3;
+  const int pairs = H * S;
+  const int pre_x = (pairs > x ? (pairs - 1 - x) / 8 + 1 : 0) * nkb_pre;
+  const int U = H * nkb_win;
+  const int win_x = U > x ? (U - 1 - x) / 8 + 1 : 0;
+  int h, kb, part;
+  if (kx < pre_x) {
+    const int pr = x + 8 * (kx / nkb_pre);
+    kb = kx % nkb_pre;
+    h = pr / S;
+    part = pr % S;
+  } else {
+    const int k2 = kx - pre_x;
+    if (k2 >= win_x) return;  // padding of this XCD's task list
+    const int u = x + 8 * k2;
+    h = u / nkb_win;
+    kb = nkb_pre + u % nkb_win;
+    part = -1;
+  }
+  const int kw0 = kb * kBK;
   const int kmax = min(N, kw0 + kBK) - 1;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -272,20 +300,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
   }
   const bool key_is_prefix = kj < Lm;
 
-  // Query rows that see some key of this workgroup.
-  int q_lo, q_hi;
+  // Query blocks whose rows see some key of this workgroup, then this part of them.
+  int b_lo, b_hi;
   if (kw0 < Lm) {
-    q_lo = full_prefix ? 0 : kw0;
-    q_hi = N;
+    b_lo = (full_prefix ? 0 : kw0) / kBQ;
+    b_hi = (N + kBQ - 1) / kBQ;
   } else {
-    q_lo = kw0;
-    q_hi = min(N, kmax + n);
+    b_lo = kw0 / kBQ;
+    b_hi = (min(N, kmax + n) + kBQ - 1) / kBQ;
   }
-  const int b_lo = q_lo / kBQ;
-  const int nblocks = (q_hi + kBQ - 1) / kBQ - b_lo;
-  // Blocks that hide no (query, key) pair: all keys in the prefix, all rows
-  // output rows, block whole.
-  const bool all_prefix_keys = kmax < Lm;
+  if (part >= 0 && S > 1) {
+    const int len = b_hi - b_lo;
+    const int s0 = b_lo + (int)((int64_t)len * part / S);
+    b_hi = b_lo + (int)((int64_t)len * (part + 1) / S);
+    b_lo = s0;
+  }
+  const int nblocks = b_hi - b_lo;
+  // Blocks that hide no (query, key) pair: all keys in the reference segment,
+  // all rows output rows, block whole.
+  int clear_lo = nblocks, clear_hi = nblocks;
+  if (kmax < Lm) {
+    clear_lo = min(nblocks, max(0, (Lm + kBQ - 1) / kBQ - b_lo));
+    clear_hi = min(nblocks, max(clear_lo, N / kBQ - b_lo));
+  }
 
   f32x16_t dk[kD / 32], dv[kD / 32];
 #pragma unroll
@@ -305,29 +342,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
   const float *lse2_h = p.lse2 + (int64_t)h * p.n_pad;
   const float *d_h = p.d_row + (int64_t)h * p.n_pad;
 
-  // DMA of one 32-row query block: wave w fills rows 8 w .. 8 w + 7 of both tiles.
-  auto dma_block = [&](int qb0, uint16_t *qt, uint16_t *gt) __attribute__((always_inline)) {
+  // DMA of one 32-row query block: wave w fills rows 8 w .. 8 w + 7 of the Q and
+  // dO tiles (4 instructions) and, with its lanes 16 w .. 16 w + 15, a quarter
+  // of the lse/D strip (1 instruction): 5 per wave and block.
+  auto dma_block = [&](int qb0, DkdvStage &st) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int row0 = 8 * wave + 4 * j;
       const int r = min(qb0 + row0 + (lane >> 4), N - 1);
       const uint32_t off = __umul24((uint32_t)r, stride);
-      dma_rows(Qg + off, lane, row0, qt);
-      dma_rows(Gg + off, lane, row0, gt);
+      dma_rows(Qg + off, lane, row0, st.q);
+      dma_rows(Gg + off, lane, row0, st.g);
+    }
+    if ((lane >> 4) == wave) {
+      const float *src = lane < 32 ? lse2_h + qb0 + lane : d_h + qb0 + (lane - 32);
+      dma4(src, lds_addr(st.ld));  // lane L's dword lands at st.ld[L]
     }
   };
 
-  auto body = [&](int bi, auto masked, auto parity) __attribute__((always_inline)) {
-    constexpr bool kMasked = decltype(masked)::value;
-    constexpr int P = decltype(parity)::value;
-    const int qb0 = (b_lo + bi) * kBQ;
-    const char *qb = reinterpret_cast<const char *>(P ? q_t1 : q_t0);
-    const char *gb = reinterpret_cast<const char *>(P ? g_t1 : g_t0);
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA of block bi landed
-    __syncthreads();
-    if (bi + 1 < nblocks) dma_block(qb0 + kBQ, P ? q_t0 : q_t1, P ? g_t0 : g_t1);
-    // S = Q K^T and dP = dO V^T: element r is query qb0 + 8 (r/4) + 4 hi + r%4, key kj.
-    f32x16_t s, dp;
+  // S = Q K^T and dP = dO V^T of the block in stage stg: element r is query
+  // qb0 + 8 (r/4) + 4 hi + r%4 of that block, key kj.
+  auto sdp = [&](int stg, f32x16_t &s, f32x16_t &dp) __attribute__((always_inline)) {
+    const char *qb = reinterpret_cast<const char *>(sm[stg].q);
+    const char *gb = reinterpret_cast<const char *>(sm[stg].g);
 #pragma unroll
     for (int ks = 0; ks < kD / 16; ++ks) {
       const bf16x8_t qa = as_bf16x8(*reinterpret_cast<const u32x4_t *>(qb + roff[ks]));
@@ -335,73 +372,134 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], ks == 0 ? f32x16_t{} : s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], ks == 0 ? f32x16_t{} : dp, 0, 0, 0);
     }
+  };
+
+  // Rows each lane's key is visible to form one interval [v_lo, v_hi): the whole
+  // sequence tail from the key (reference-segment key), plus every row below
+  // L_m with the full-prefix mode, or the n rows from the key (output key).
+  int v_lo = kj, v_hi = key_is_prefix ? N : min(N, kj + n);
+  if (key_is_prefix && full_prefix) v_lo = 0;
+  if (!k_ok) v_hi = v_lo;
+  const uint32_t v_span = (uint32_t)(v_hi - v_lo);
+
+  // One pipeline step for block bi (in stage bi & 3), whose S and dP were
+  // computed the step before: wait for block bi + 1, start the DMA of block
+  // bi + 3, then S/dP of block bi + 1 on the matrix cores while this block's P
+  // and dS are formed, then dV += P^T dO and dK += dS^T Q.
+  auto step = [&](int bi, f32x16_t &s_cur, f32x16_t &dp_cur, f32x16_t &s_nxt, f32x16_t &dp_nxt)
+      __attribute__((always_inline)) {
+    const int qb0 = (b_lo + bi) * kBQ;
+    const DkdvStage &st = sm[bi & 3];
+    // Loads return in order: with only block bi + 2's five outstanding, this
+    // wave's part of block bi + 1 has landed.
+    if (bi + 2 < nblocks)
+      wait_vmcnt<5>();
+    else
+      wait_vmcnt<0>();
+    block_barrier();  // every wave's part landed; stage (bi + 3) & 3 is no longer read
+    if (bi + 3 < nblocks) dma_block(qb0 + 3 * kBQ, sm[(bi + 3) & 3]);
+    float xs[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xs[r] = s_cur[r];
+    if (bi < clear_lo || bi >= clear_hi) {
+      const uint32_t t = (uint32_t)(qb0 + 4 * hi - v_lo);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        xs[r] = t + (uint32_t)(8 * (r >> 2) + (r & 3)) < v_span ? xs[r] : kNegInf;
+    }
+    // Unconditional so that it shares one scheduling region with the VALU work
+    // below; after the last block it reads a stale stage and the result is unused.
+    sdp((bi + 1) & 3, s_nxt, dp_nxt);
     // P and dS for this lane's key and 16 queries, in 4 groups of 4 consecutive rows.
     uint32_t pw[8], dw[8];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int i0 = qb0 + 8 * g + 4 * hi;
-      const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(lse2_h + i0);
-      const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(d_h + i0);
+      const int r0 = 8 * g + 4 * hi;
+      const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(&st.ld[r0]);
+      const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(&st.ld[kBQ + r0]);
       float pv[4], dsv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g + e;
-        float x = s[r];
-        if constexpr (kMasked) {
-          const int i = i0 + e;
-          bool vis = i < N && k_ok && kj <= i;
-          if (key_is_prefix) {
-            vis = vis || (i < N && k_ok && full_prefix && i < Lm);  // full prefix: rows < L_m see the prefix
-          } else {
-            vis = vis && i - kj < n;
-          }
-          x = vis ? x : kNegInf;
-        }
-        pv[e] = __builtin_amdgcn_exp2f(fmaf(x, c, -l4[e]));
-        dsv[e] = pv[e] * (dp[r] - d4[e]);
+        pv[e] = __builtin_amdgcn_exp2f(fmaf(xs[4 * g + e], c, -l4[e]));
+        dsv[e] = pv[e] * (dp_cur[4 * g + e] - d4[e]);
       }
       pw[2 * g] = pack_bf16(pv[0], pv[1]);
       pw[2 * g + 1] = pack_bf16(pv[2], pv[3]);
       dw[2 * g] = pack_bf16(dsv[0], dsv[1]);
       dw[2 * g + 1] = pack_bf16(dsv[2], dsv[3]);
     }
-    // dV += P^T dO and dK += dS^T Q over two 16-query steps; step st uses
-    // elements 8 st .. 8 st + 7 (queries 16 st + {4 hi.., 8 + 4 hi..}).
+    // dV += P^T dO and dK += dS^T Q over two 16-query steps; step st2 uses
+    // elements 8 st2 .. 8 st2 + 7 (queries 16 st2 + {4 hi.., 8 + 4 hi..}).
+    const char *qb = reinterpret_cast<const char *>(st.q);
+    const char *gb = reinterpret_cast<const char *>(st.g);
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const bf16x8_t pa = as_bf16x8(u32x4_t{pw[4 * st], pw[4 * st + 1], pw[4 * st + 2], pw[4 * st + 3]});
-      const bf16x8_t da = as_bf16x8(u32x4_t{dw[4 * st], dw[4 * st + 1], dw[4 * st + 2], dw[4 * st + 3]});
+    for (int st2 = 0; st2 < 2; ++st2) {
+      const bf16x8_t pa = as_bf16x8(u32x4_t{pw[4 * st2], pw[4 * st2 + 1], pw[4 * st2 + 2], pw[4 * st2 + 3]});
+      const bf16x8_t da = as_bf16x8(u32x4_t{dw[4 * st2], dw[4 * st2 + 1], dw[4 * st2 + 2], dw[4 * st2 + 3]});
 #pragma unroll
       for (int db = 0; db < kD / 32; ++db) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, tr_operand(gb, toff[db][0], toff[db][1], st),
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, tr_operand(gb, toff[db][0], toff[db][1], st2),
                                                          dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, tr_operand(qb, toff[db][0], toff[db][1], st),
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, tr_operand(qb, toff[db][0], toff[db][1], st2),
                                                          dk[db], 0, 0, 0);
       }
     }
-  };
-  auto step = [&](int bi, auto masked) __attribute__((always_inline)) {
-    if (bi & 1)
-      body(bi, masked, std::integral_constant<int, 1>{});
-    else
-      body(bi, masked, std::integral_constant<int, 0>{});
+    // Interleave: the look-ahead S/dP products (16 MFMA, 16 LDS reads) with this
+    // block's P/dS arithmetic, then the dV/dK products with their transposing reads.
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+    }
   };
 
-  if (nblocks > 0) dma_block(b_lo * kBQ, q_t0, g_t0);
-  __builtin_amdgcn_s_waitcnt(0);
-  // Unmasked run: blocks inside [L_m, N), whole, when every key is a prefix key.
-  int clear_lo = nblocks, clear_hi = nblocks;
-  if (all_prefix_keys) {
-    clear_lo = max(0, (Lm + kBQ - 1) / kBQ - b_lo);
-    clear_hi = max(clear_lo, N / kBQ - b_lo);
+  wait_vmcnt<0>();  // resident K/V rows landed (the compiler does not count the DMA)
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    if (j < nblocks) dma_block((b_lo + j) * kBQ, sm[j]);
+  f32x16_t sa = {}, dpa = {}, sb = {}, dpb = {};
+  if (nblocks > 0) {
+    // block 0 landed: blocks 1 and 2 (five instructions each) may be outstanding
+    if (nblocks > 2)
+      wait_vmcnt<10>();
+    else if (nblocks > 1)
+      wait_vmcnt<5>();
+    else
+      wait_vmcnt<0>();
+    block_barrier();
+    sdp(0, sa, dpa);
   }
   int bi = 0;
-  for (; bi < clear_lo; ++bi) step(bi, std::true_type{});
-  for (; bi < clear_hi; ++bi) step(bi, std::false_type{});
-  for (; bi < nblocks; ++bi) step(bi, std::true_type{});
+  for (; bi + 1 < nblocks; bi += 2) {
+    step(bi, sa, dpa, sb, dpb);
+    step(bi + 1, sb, dpb, sa, dpa);
+  }
+  if (bi < nblocks) step(bi, sa, dpa, sb, dpb);
 
   // Accumulator element r of dk[db] is key kw0 + 32 wave + 8 (r/4) + 4 hi + r%4
   // and d = 32 db + l32: every lane stores, whatever its own score column.
+  if (part >= 0 && S > 1) {
+    const int64_t base = (((int64_t)part * H + h) * p.kpre + kw0 + 32 * wave) * kD;
+    float *pk = p.part_dk + base;
+    float *pv = p.part_dv + base;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kl = 8 * (r >> 2) + 4 * hi + (r & 3);
+#pragma unroll
+      for (int db = 0; db < kD / 32; ++db) {
+        pk[kl * kD + 32 * db + l32] = dk[db][r];
+        pv[kl * kD + 32 * db + l32] = dv[db][r];
+      }
+    }
+    return;
+  }
   const float sc = p.scale;
   uint16_t *dkg = static_cast<uint16_t *>(p.dk) + (int64_t)h * kD;
   uint16_t *dvg = static_cast<uint16_t *>(p.dv) + (int64_t)h * kD;
@@ -418,7 +516,40 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
   }
 }
 
+// Sums the parts' fp32 partials of the reference-segment key blocks and stores
+// dK (times the scale) and dV in bf16. One thread per (key, head, 8 dims).
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(MaskedBwdParams p) {
+  const int H = p.heads;
+  const int kval = min(p.seq_len, p.kpre);
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (int64_t)kval * H * 16) return;
+  const int c = (int)(t & 15);
+  const int64_t kh = t >> 4;
+  const int h = (int)(kh % H), key = (int)(kh / H);
+  f32x4_t a0 = {}, a1 = {}, b0 = {}, b1 = {};
+  for (int s = 0; s < p.parts; ++s) {
+    const int64_t off = (((int64_t)s * H + h) * p.kpre + key) * kD + 8 * c;
+    a0 += *reinterpret_cast<const f32x4_t *>(p.part_dk + off);
+    a1 += *reinterpret_cast<const f32x4_t *>(p.part_dk + off + 4);
+    b0 += *reinterpret_cast<const f32x4_t *>(p.part_dv + off);
+    b1 += *reinterpret_cast<const f32x4_t *>(p.part_dv + off + 4);
+  }
+  const float sc = p.scale;
+  const int64_t o = ((int64_t)key * H + h) * kD + 8 * c;
+  *reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(p.dk) + o) =
+      u32x4_t{pack_bf16(a0[0] * sc, a0[1] * sc), pack_bf16(a0[2] * sc, a0[3] * sc),
+              pack_bf16(a1[0] * sc, a1[1] * sc), pack_bf16(a1[2] * sc, a1[3] * sc)};
+  *reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(p.dv) + o) =
+      u32x4_t{pack_bf16(b0[0], b0[1]), pack_bf16(b0[2], b0[3]), pack_bf16(b1[0], b1[1]),
+              pack_bf16(b1[2], b1[3])};
+}
+
 }  // namespace
+
+int64_t masked_bwd_dkdv_grid(int32_t heads, int32_t parts, int32_t nkb_pre, int32_t nkb_win) {
+  const int64_t pairs = (int64_t)heads * parts, u = (int64_t)heads * nkb_win;
+  return 8 * (((pairs + 7) / 8) * nkb_pre + (u + 7) / 8);
+}
 
 hipError_t launch_masked_bwd(const MaskedBwdParams &p, hipStream_t s) {
   const int64_t rows = (int64_t)p.heads * p.n_pad;
@@ -429,8 +560,13 @@ hipError_t launch_masked_bwd(const MaskedBwdParams &p, hipStream_t s) {
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)gq), dim3(256), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t gk = (int64_t)((p.seq_len + kBK - 1) / kBK) * p.heads;
+  const int64_t gk = masked_bwd_dkdv_grid(p.heads, p.parts, p.nkb_pre, p.nkb_win);
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)gk), dim3(256), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess || p.parts == 1 || p.nkb_pre == 0) return e;
+  const int64_t kval = p.seq_len < p.kpre ? p.seq_len : p.kpre;
+  const int64_t threads = kval * p.heads * 16;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

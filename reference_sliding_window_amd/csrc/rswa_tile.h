@@ -66,15 +66,60 @@ __device__ __forceinline__ bf16x8_t tr_operand(const char *tile, uint32_t off0, 
   return as_bf16x8(u32x4_t{a0.x, a0.y, a1.x, a1.y});
 }
 
+// LDS DMA (global_load_lds_*) is issued from inline asm so that the compiler
+// does not track it: tracked, it makes every transposing LDS read (whose memory
+// operand carries no alias information) wait for all DMA in flight, which
+// defeats prefetching. The instruction has no register outputs. Callers order
+// DMA writes before LDS reads themselves: s_waitcnt vmcnt on the issuing wave,
+// then block_barrier(). The LDS base goes in M0 (one wait state before use).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void_t *)p));
+}
+
+// M0 is saved and restored around the instruction: the compiler reserves it.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+
+__device__ __forceinline__ void dma4(const void *src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+
+// Workgroup barrier with no memory fence of its own (a fence would wait for all
+// DMA in flight); the compiler may not move memory accesses across it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt with only vmcnt = n (n < 16); expcnt and lgkmcnt left at their maximum.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | n);
+}
+
 // One DMA instruction (global_load_lds_dwordx4): 64 lanes x 16 bytes land at
 // tile + row0 * 256 + 16 lane, i.e. rows row0 .. row0 + 3, physical chunk
-// lane % 16. Lane L loads global row `grow` (already clamped by the caller), logical
-// chunk (L % 16) ^ chunk_swz(row0 + L / 16).
+// lane % 16. Lane L loads global row `src_row` (already clamped by the caller),
+// logical chunk (L % 16) ^ chunk_swz(row0 + L / 16).
 __device__ __forceinline__ void dma_rows(const uint16_t *src_row, int lane, int row0, uint16_t *tile) {
   const int r = row0 + (lane >> 4);
   const int c = (lane & 15) ^ chunk_swz(r);
-  char *dst = reinterpret_cast<char *>(tile) + row0 * kRowBytes;
-  __builtin_amdgcn_global_load_lds(src_row + 8 * c, (lds_void_t *)dst, 16, 0, 0);
+  dma16(src_row + 8 * c, lds_addr(reinterpret_cast<char *>(tile) + row0 * kRowBytes));
 }
 
 }  // namespace tile

@@ -134,17 +134,25 @@ def test_masked_argument_checks():
 
 
 def test_masked_bwd_workspace_size():
-    assert rs.rswa_masked_bwd_workspace_size(-1, 2) == 0
-    assert rs.rswa_masked_bwd_workspace_size(10, 0) == 0
-    assert rs.rswa_masked_bwd_workspace_size(0, 2) == 0
-    # two float arrays [H][roundup(N, 32)]
-    assert rs.rswa_masked_bwd_workspace_size(1, 2) == 2 * 2 * 32 * 4
-    assert rs.rswa_masked_bwd_workspace_size(32768, 16) == 2 * 16 * 32768 * 4
-    assert rs.rswa_masked_bwd_workspace_size(300, 3) == 2 * 3 * 320 * 4
+    ws = rs.rswa_masked_bwd_workspace_size
+    assert ws(-1, 0, 2) == 0
+    assert ws(10, 0, 0) == 0
+    assert ws(10, 11, 2) == 0          # ref_len > seq_len
+    assert ws(10, 5, 2, -1) == 0
+    assert ws(10, 5, 2, 65) == 0
+    assert ws(0, 0, 2) == 0
+    # one part: two float arrays [H][roundup(N, 32)]
+    assert ws(1, 1, 2, 1) == 2 * 2 * 32 * 4
+    assert ws(300, 40, 3, 1) == 2 * 3 * 320 * 4
+    # parts > 1 add fp32 partial dK and dV for the 128-key blocks below ref_len
+    assert ws(300, 40, 3, 4) == 2 * 3 * 320 * 4 + 2 * 4 * 3 * 128 * 128 * 4
+    assert ws(300, 0, 3, 4) == 2 * 3 * 320 * 4    # no reference segment: nothing to split
+    # the library's choice at the packed 32K shape: runs of about 256 query blocks
+    assert ws(32768, 4128, 16) == 2 * 16 * 32768 * 4 + 2 * 4 * 16 * 4224 * 128 * 4
 
 
 def test_masked_bwd_argument_checks():
-    ws = rs.rswa_masked_bwd_workspace_size(300, 2)
+    ws = rs.rswa_masked_bwd_workspace_size(300, 40, 2)
     base = dict(q=A, k=A, v=A, out=A, dout=A, lse=A, dq=A, dk=A, dv=A, seq_len=300, ref_len=40,
                 window=8, num_heads=2, head_dim=128, workspace=A, workspace_bytes=ws)
     b = lambda **kw: rs.rswa_masked_attn_bwd(**{**base, **kw}, check=False)
@@ -165,6 +173,9 @@ def test_masked_bwd_argument_checks():
     assert b(workspace=None, workspace_bytes=0) == rs.RSWA_ERR_NULL
     assert b(workspace_bytes=ws - 1) == rs.RSWA_ERR_WORKSPACE
     assert b(workspace=A + 4) == rs.RSWA_ERR_ALIGN
+    assert b(num_parts=-1) == rs.RSWA_ERR_SHAPE
+    assert b(num_parts=65) == rs.RSWA_ERR_SHAPE
+    assert b(num_parts=3) == rs.RSWA_ERR_WORKSPACE   # more parts need more workspace
     assert b(seq_len=0, ref_len=0, workspace=None, workspace_bytes=0) == rs.RSWA_OK
 
 

@@ -45,7 +45,7 @@ def check_grad(got, ref, what):
 class PackedRun:
     """Forward (with lse) and backward of one packed sequence on the device."""
 
-    def __init__(self, N, L_m, n, H, mode, seed, sigma=1.0):
+    def __init__(self, N, L_m, n, H, mode, seed, sigma=1.0, parts=0):
         self.mw = wl.MaskedWorkload("masked-bwd", seq_len=N, heads=H, head_dim=128, ref_len=L_m,
                                     window=n, dtype="bf16", sigma=sigma, base_seed=seed)
         self.N, self.L_m, self.n, self.H, self.mode = N, L_m, n, H, mode
@@ -58,7 +58,8 @@ class PackedRun:
         self.dq = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
         self.dk = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
         self.dv = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
-        nbytes = rs.rswa_masked_bwd_workspace_size(N, H)
+        self.parts = parts
+        nbytes = rs.rswa_masked_bwd_workspace_size(N, L_m, H, parts)
         self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
 
     def forward(self):
@@ -68,7 +69,7 @@ class PackedRun:
     def backward(self):
         rs.rswa_masked_attn_bwd(self.Qd, self.Kd, self.Vd, self.out, self.Gd, self.lse, self.dq, self.dk,
                                 self.dv, self.N, self.L_m, self.n, self.H, 128, rs.RSWA_BF16, self.mode,
-                                0.0, self.ws)
+                                0.0, self.ws, num_parts=self.parts)
 
     def f64(self):
         f = lambda a: wl.to_f64(a, "bf16")
@@ -127,6 +128,45 @@ def test_backward_small_every_row_and_key(N, L_m, n, mode):
     check_grad(to_f64(r.dq), dQ, f"dQ {tag}")
     check_grad(to_f64(r.dk), dK, f"dK {tag}")
     check_grad(to_f64(r.dv), dV, f"dV {tag}")
+
+
+@pytest.mark.parametrize("N,L_m,n,mode,parts", [
+    (300, 40, 8, CAUSAL, 2),
+    (700, 300, 200, FULL, 3),
+    (513, 130, 128, CAUSAL, 7),
+    (200, 200, 4, CAUSAL, 64),   # more parts than query blocks: empty runs
+    (1, 1, 128, CAUSAL, 5),
+])
+def test_backward_split_walks_every_row_and_key(N, L_m, n, mode, parts):
+    """Reference-segment keys with their row walks cut into parts (fp32 partials
+    summed by the reduction kernel)."""
+    banner(f"packed bwd parts={parts} N={N} L_m={L_m} n={n} mode={mode}")
+    r = PackedRun(N, L_m, n, 2, mode, seed=7000 + N + L_m + n + mode, parts=parts)
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    Q, K, V, G = r.f64()
+    dQ, dK, dV = orc.masked_attention_backward(Q, K, V, G, L_m, n, r.mw.scale, mode)
+    tag = f"parts={parts} N={N} L_m={L_m} n={n} mode={mode}"
+    check_grad(to_f64(r.dq), dQ, f"dQ {tag}")
+    check_grad(to_f64(r.dk), dK, f"dK {tag}")
+    check_grad(to_f64(r.dv), dV, f"dV {tag}")
+
+
+def test_backward_parts_change_only_rounding():
+    """One walk against several: the same gradients up to fp32 summation order."""
+    banner("packed bwd parts invariance")
+    runs = []
+    for parts in (1, 4):
+        r = PackedRun(2048, 700, 128, 2, CAUSAL, seed=99, parts=parts)
+        r.forward()
+        r.backward()
+        torch.cuda.synchronize()
+        runs.append([to_f64(t) for t in (r.dq, r.dk, r.dv)])
+    for name, a, b in zip(("dQ", "dK", "dV"), *runs):
+        check_grad(b, a, f"{name} parts 4 vs 1")
+        if name == "dQ":
+            assert np.array_equal(a, b)  # dQ does not depend on the split
 
 
 def test_backward_is_deterministic():
