@@ -66,29 +66,17 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(MaskedBwdParams p) {
 }
 
 // --------------------------------------------------------------- dQ kernel
-constexpr int kBMq = 128;  // query rows per workgroup
-constexpr int kBNq = 64;   // keys per block (two 32-key tiles)
+constexpr int kBMq = 128;    // query rows per workgroup (4 waves x 32)
+constexpr int kBNq = 32;     // keys per block
+constexpr int kStagesQ = 4;  // LDS ring of key blocks: one in use, one computed ahead, two in flight
 
-struct KBlock {
-  int kb0, kend;
+struct DqStage {
+  uint16_t k[kBNq * kD];
+  uint16_t v[kBNq * kD];
 };
 
-// Sets to -inf the scores of keys hidden from query qi (S^T layout: element r
-// of a 32-key tile is key kt0 + 8 (r/4) + 4 hi + r%4 for this lane's query).
-template <bool kWindow>
-__device__ __forceinline__ void mask_st(f32x16_t &s, int kt0, int kend, int qi, int n,
-                                        bool sees_prefix, int hi) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int j = kt0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-    const bool vis = kWindow ? (j < kend && j <= qi && qi - j < n)
-                             : (j < kend && (sees_prefix || j <= qi));
-    s[r] = vis ? s[r] : kNegInf;
-  }
-}
-
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(MaskedBwdParams p) {
-  __shared__ uint16_t k_t0[kBNq * kD], k_t1[kBNq * kD], v_t0[kBNq * kD], v_t1[kBNq * kD];
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(MaskedBwdParams p) {
+  __shared__ DqStage sm[kStagesQ];
   const int N = p.seq_len, H = p.heads, Lm = p.ref_len, n = p.window;
   const bool full_prefix = p.prefix_mode == RSWA_PREFIX_FULL;
   const int nqb = (N + kBMq - 1) / kBMq;
@@ -107,20 +95,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(MaskedBwdParams p) {
   const uint16_t *Vg = static_cast<const uint16_t *>(p.v) + (int64_t)h * kD;
   const uint16_t *Gg = static_cast<const uint16_t *>(p.dout) + (int64_t)h * kD;
 
+  // Key blocks: the reference segment [0, pre_hi), then the output keys
+  // [win_lo, win_hi) some row of this workgroup sees.
   const int pre_hi = (full_prefix && q0 < Lm) ? Lm : min(Lm, q_end);
   const int win_lo = max(Lm, max(q0, Lm) - n + 1);
   const int win_hi = q_end > Lm ? q_end : win_lo;
   const int nb_pre = (pre_hi + kBNq - 1) / kBNq;
   const int nblocks = nb_pre + (win_hi - win_lo + kBNq - 1) / kBNq;
-  auto block_of = [&](int bi) __attribute__((always_inline)) -> KBlock {
-    if (bi < nb_pre) return {bi * kBNq, pre_hi};
-    return {win_lo + (bi - nb_pre) * kBNq, win_hi};
+  auto kb0_of = [&](int bi) __attribute__((always_inline)) {
+    return bi < nb_pre ? bi * kBNq : win_lo + (bi - nb_pre) * kBNq;
   };
+  auto kend_of = [&](int bi) __attribute__((always_inline)) { return bi < nb_pre ? pre_hi : win_hi; };
 
   const int qw0 = q0 + wave * 32;
   const int qi = qw0 + l32;
   const bool q_ok = qi < N;
-  const bool sees_prefix = qi >= Lm || full_prefix;
   bf16x8_t qf[kD / 16], gf[kD / 16];
   {
     const int64_t r = (int64_t)(q_ok ? qi : 0) * stride;
@@ -136,6 +125,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(MaskedBwdParams p) {
   const float Dq = p.d_row[rq];
   const float c = p.scale_log2;
 
+  // The keys row qi sees inside each segment form one interval [lo, lo + span):
+  // the reference segment up to L_m (or up to the row itself for a causal row
+  // below L_m), and the n output keys ending at the row.
+  const int pv = (full_prefix || qi >= Lm) ? Lm : qi + 1;
+  const uint32_t span_p = (uint32_t)pv;
+  const int lo_w = max(Lm, qi - n + 1);
+  const uint32_t span_w = (uint32_t)max(0, qi + 1 - lo_w);
+  // Reference-segment blocks no row of this wave masks.
+  const int nb_clear = min((!full_prefix && qw0 < Lm) ? qw0 + 1 : Lm, pre_hi) / kBNq;
+
   f32x16_t dq[kD / 32];
 #pragma unroll
   for (int j = 0; j < kD / 32; ++j) dq[j] = f32x16_t{};
@@ -149,73 +148,118 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(MaskedBwdParams p) {
     toff[db][1] = tr_off(lane, db, 1);
   }
 
-  // DMA of one 64-key block: wave w fills rows 16 w .. 16 w + 15 of both tiles.
-  auto dma_block = [&](const KBlock &bk, uint16_t *kt, uint16_t *vt) __attribute__((always_inline)) {
+  // DMA of one 32-key block: wave w fills rows 8 w .. 8 w + 7 of the K and V
+  // tiles, 4 instructions per wave and block.
+  auto dma_block = [&](int bi, DqStage &st) __attribute__((always_inline)) {
+    const int kb0 = kb0_of(bi), kend = kend_of(bi);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row0 = 16 * wave + 4 * j;
-      const int r = min(bk.kb0 + row0 + (lane >> 4), bk.kend - 1);
+    for (int j = 0; j < 2; ++j) {
+      const int row0 = 8 * wave + 4 * j;
+      const int r = min(kb0 + row0 + (lane >> 4), kend - 1);
       const uint32_t off = __umul24((uint32_t)r, stride);
-      dma_rows(Kg + off, lane, row0, kt);
-      dma_rows(Vg + off, lane, row0, vt);
+      dma_rows(Kg + off, lane, row0, st.k);
+      dma_rows(Vg + off, lane, row0, st.v);
     }
   };
 
-  auto body = [&](int bi, auto mode, auto parity) __attribute__((always_inline)) {
-    constexpr int kMode = decltype(mode)::value;
-    constexpr int P = decltype(parity)::value;
-    const KBlock bk = block_of(bi);
-    const char *kb = reinterpret_cast<const char *>(P ? k_t1 : k_t0);
-    const char *vb = reinterpret_cast<const char *>(P ? v_t1 : v_t0);
-    wait_vmcnt<0>();  // this wave's DMA of block bi landed
-    block_barrier();  // every wave's did; the other buffer is no longer read
-    if (bi + 1 < nblocks) dma_block(block_of(bi + 1), P ? k_t0 : k_t1, P ? v_t0 : v_t1);
+  // S^T = K Q^T and dP^T = V dO^T of the block in stage stg: element r is key
+  // kb0 + 8 (r/4) + 4 hi + r%4 of that block, query qi.
+  auto sdp = [&](int stg, f32x16_t &s, f32x16_t &dp) __attribute__((always_inline)) {
+    const char *kb = reinterpret_cast<const char *>(sm[stg].k);
+    const char *vb = reinterpret_cast<const char *>(sm[stg].v);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      f32x16_t s, dp;
-#pragma unroll
-      for (int ks = 0; ks < kD / 16; ++ks) {
-        const bf16x8_t ka = as_bf16x8(*reinterpret_cast<const u32x4_t *>(kb + koff[ks] + kt * 32 * kRowBytes));
-        const bf16x8_t va = as_bf16x8(*reinterpret_cast<const u32x4_t *>(vb + koff[ks] + kt * 32 * kRowBytes));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? f32x16_t{} : s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], ks == 0 ? f32x16_t{} : dp, 0, 0, 0);
-      }
-      if constexpr (kMode == 1) mask_st<false>(s, bk.kb0 + 32 * kt, bk.kend, qi, n, sees_prefix, hi);
-      if constexpr (kMode == 2) mask_st<true>(s, bk.kb0 + 32 * kt, bk.kend, qi, n, sees_prefix, hi);
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        uint32_t w4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r0 = 8 * half + 2 * e;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r0], c, -lse2));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r0 + 1], c, -lse2));
-          w4[e] = pack_bf16(p0 * (dp[r0] - Dq), p1 * (dp[r0 + 1] - Dq));
-        }
-        const bf16x8_t dsb = as_bf16x8(u32x4_t{w4[0], w4[1], w4[2], w4[3]});
-        const int st = 2 * kt + half;
-#pragma unroll
-        for (int db = 0; db < kD / 32; ++db)
-          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(kb, toff[db][0], toff[db][1], st),
-                                                           dsb, dq[db], 0, 0, 0);
-      }
+    for (int ks = 0; ks < kD / 16; ++ks) {
+      const bf16x8_t ka = as_bf16x8(*reinterpret_cast<const u32x4_t *>(kb + koff[ks]));
+      const bf16x8_t va = as_bf16x8(*reinterpret_cast<const u32x4_t *>(vb + koff[ks]));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? f32x16_t{} : s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], ks == 0 ? f32x16_t{} : dp, 0, 0, 0);
     }
   };
-  auto step = [&](int bi, auto mode) __attribute__((always_inline)) {
-    if (bi & 1)
-      body(bi, mode, std::integral_constant<int, 1>{});
+
+  // One pipeline step for block bi (stage bi & 3), its S^T and dP^T computed the
+  // step before: wait for block bi + 1, start the DMA of block bi + 3, then
+  // S^T/dP^T of block bi + 1 interleaved (hand-ordered) with this block's dS,
+  // then dQ^T += K^T dS^T.
+  auto step = [&](int bi, f32x16_t &s_cur, f32x16_t &dp_cur, f32x16_t &s_nxt, f32x16_t &dp_nxt)
+      __attribute__((always_inline)) {
+    const DqStage &st = sm[bi & 3];
+    if (bi + 2 < nblocks)
+      wait_vmcnt<4>();  // only block bi + 2's four may be outstanding
     else
-      body(bi, mode, std::integral_constant<int, 0>{});
+      wait_vmcnt<0>();
+    block_barrier();  // every wave's part of block bi + 1 landed; stage (bi + 3) & 3 is free
+    if (bi + 3 < nblocks) dma_block(bi + 3, sm[(bi + 3) & 3]);
+    float xs[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xs[r] = s_cur[r];
+    if (bi >= nb_clear) {
+      const bool win = bi >= nb_pre;
+      const uint32_t t = (uint32_t)(kb0_of(bi) + 4 * hi - (win ? lo_w : 0));
+      const uint32_t span = win ? span_w : span_p;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        xs[r] = t + (uint32_t)(8 * (r >> 2) + (r & 3)) < span ? xs[r] : kNegInf;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const char *kn = reinterpret_cast<const char *>(sm[(bi + 1) & 3].k);
+    const char *vn = reinterpret_cast<const char *>(sm[(bi + 1) & 3].v);
+    bf16x8_t ka[kD / 16], va[kD / 16];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      ka[ks] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(kn + koff[ks]));
+      va[ks] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(vn + koff[ks]));
+    }
+    uint32_t dw[8];
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) {
+      if (ks + 2 < kD / 16) {
+        ka[ks + 2] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(kn + koff[ks + 2]));
+        va[ks + 2] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(vn + koff[ks + 2]));
+      }
+      s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], ks == 0 ? f32x16_t{} : s_nxt, 0, 0, 0);
+      dp_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], gf[ks], ks == 0 ? f32x16_t{} : dp_nxt, 0, 0, 0);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(xs[2 * ks], c, -lse2));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(xs[2 * ks + 1], c, -lse2));
+      dw[ks] = pack_bf16(p0 * (dp_cur[2 * ks] - Dq), p1 * (dp_cur[2 * ks + 1] - Dq));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dQ^T += K^T dS^T over two 16-key halves (elements 8 half .. 8 half + 7);
+    // transposing reads of K one product ahead.
+    const char *kb = reinterpret_cast<const char *>(st.k);
+    bf16x8_t tk[2];
+    tk[0] = tr_operand(kb, toff[0][0], toff[0][1], 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int half = j >> 2, db = j & 3;
+      if (j + 1 < 8) tk[(j + 1) & 1] = tr_operand(kb, toff[(j + 1) & 3][0], toff[(j + 1) & 3][1], (j + 1) >> 2);
+      const bf16x8_t dsb = as_bf16x8(u32x4_t{dw[4 * half], dw[4 * half + 1], dw[4 * half + 2], dw[4 * half + 3]});
+      dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tk[j & 1], dsb, dq[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   wait_vmcnt<0>();  // resident Q/dO rows landed (the compiler does not count the DMA)
-  if (nblocks > 0) dma_block(block_of(0), k_t0, v_t0);
-  int nb_clear = pre_hi / kBNq;
-  if (!full_prefix && qw0 < Lm) nb_clear = min(nb_clear, (qw0 + 1) / kBNq);
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    if (j < nblocks) dma_block(j, sm[j]);
+  f32x16_t sa = {}, dpa = {}, sb = {}, dpb = {};
+  if (nblocks > 0) {
+    // block 0 landed: blocks 1 and 2 (four instructions each) may be outstanding
+    if (nblocks > 2)
+      wait_vmcnt<8>();
+    else if (nblocks > 1)
+      wait_vmcnt<4>();
+    else
+      wait_vmcnt<0>();
+    block_barrier();
+    sdp(0, sa, dpa);
+  }
   int bi = 0;
-  for (; bi < nb_clear; ++bi) step(bi, std::integral_constant<int, 0>{});
-  for (; bi < nb_pre; ++bi) step(bi, std::integral_constant<int, 1>{});
-  for (; bi < nblocks; ++bi) step(bi, std::integral_constant<int, 2>{});
+  for (; bi + 1 < nblocks; bi += 2) {
+    step(bi, sa, dpa, sb, dpb);
+    step(bi + 1, sb, dpb, sa, dpa);
+  }
+  if (bi < nblocks) step(bi, sa, dpa, sb, dpb);
 
   if (!q_ok) return;
   // dQ^T accumulator element r of dq[db] is d = 32 db + 8 (r/4) + 4 hi + r%4.
@@ -384,8 +428,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
 
   // One pipeline step for block bi (in stage bi & 3), whose S and dP were
   // computed the step before: wait for block bi + 1, start the DMA of block
-  // bi + 3, then S/dP of block bi + 1 on the matrix cores while this block's P
-  // and dS are formed, then dV += P^T dO and dK += dS^T Q.
+  // bi + 3, then S/dP of block bi + 1 on the matrix cores interleaved with this
+  // block's P and dS (two elements per k-step, about the two products' time),
+  // then dV += P^T dO and dK += dS^T Q. The order is fixed by hand
+  // (sched_barrier): the compiler's own schedule serialises the two units.
   auto step = [&](int bi, f32x16_t &s_cur, f32x16_t &dp_cur, f32x16_t &s_nxt, f32x16_t &dp_nxt)
       __attribute__((always_inline)) {
     const int qb0 = (b_lo + bi) * kBQ;
@@ -407,56 +453,61 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
       for (int r = 0; r < 16; ++r)
         xs[r] = t + (uint32_t)(8 * (r >> 2) + (r & 3)) < v_span ? xs[r] : kNegInf;
     }
-    // Unconditional so that it shares one scheduling region with the VALU work
-    // below; after the last block it reads a stale stage and the result is unused.
-    sdp((bi + 1) & 3, s_nxt, dp_nxt);
-    // P and dS for this lane's key and 16 queries, in 4 groups of 4 consecutive rows.
-    uint32_t pw[8], dw[8];
+    __builtin_amdgcn_sched_barrier(0);
+    // lse/D of this block's rows 8 g + 4 hi .. + 3 (broadcast reads).
+    f32x4_t l4[4], d4[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int r0 = 8 * g + 4 * hi;
-      const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(&st.ld[r0]);
-      const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(&st.ld[kBQ + r0]);
-      float pv[4], dsv[4];
+      l4[g] = *reinterpret_cast<const f32x4_t *>(&st.ld[8 * g + 4 * hi]);
+      d4[g] = *reinterpret_cast<const f32x4_t *>(&st.ld[kBQ + 8 * g + 4 * hi]);
+    }
+    // S/dP of block bi + 1 (a stale stage after the last block; result unused).
+    const char *qn = reinterpret_cast<const char *>(sm[(bi + 1) & 3].q);
+    const char *gn = reinterpret_cast<const char *>(sm[(bi + 1) & 3].g);
+    bf16x8_t qa[kD / 16], ga[kD / 16];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pv[e] = __builtin_amdgcn_exp2f(fmaf(xs[4 * g + e], c, -l4[e]));
-        dsv[e] = pv[e] * (dp_cur[4 * g + e] - d4[e]);
+    for (int ks = 0; ks < 2; ++ks) {
+      qa[ks] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(qn + roff[ks]));
+      ga[ks] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(gn + roff[ks]));
+    }
+    uint32_t pw[8], dw[8];
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) {
+      if (ks + 2 < kD / 16) {
+        qa[ks + 2] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(qn + roff[ks + 2]));
+        ga[ks + 2] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(gn + roff[ks + 2]));
       }
-      pw[2 * g] = pack_bf16(pv[0], pv[1]);
-      pw[2 * g + 1] = pack_bf16(pv[2], pv[3]);
-      dw[2 * g] = pack_bf16(dsv[0], dsv[1]);
-      dw[2 * g + 1] = pack_bf16(dsv[2], dsv[3]);
+      s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], ks == 0 ? f32x16_t{} : s_nxt, 0, 0, 0);
+      dp_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[ks], vf[ks], ks == 0 ? f32x16_t{} : dp_nxt, 0, 0, 0);
+      // elements 2 ks, 2 ks + 1: rows 8 (ks/2) + 4 hi + 2 (ks%2) + {0, 1}
+      const int g = ks >> 1, e = 2 * (ks & 1);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(xs[2 * ks], c, -l4[g][e]));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(xs[2 * ks + 1], c, -l4[g][e + 1]));
+      pw[ks] = pack_bf16(p0, p1);
+      dw[ks] = pack_bf16(p0 * (dp_cur[2 * ks] - d4[g][e]), p1 * (dp_cur[2 * ks + 1] - d4[g][e + 1]));
+      __builtin_amdgcn_sched_barrier(0);
     }
     // dV += P^T dO and dK += dS^T Q over two 16-query steps; step st2 uses
     // elements 8 st2 .. 8 st2 + 7 (queries 16 st2 + {4 hi.., 8 + 4 hi..}).
+    // Transposing reads run one (st2, db) pair ahead of their products.
     const char *qb = reinterpret_cast<const char *>(st.q);
     const char *gb = reinterpret_cast<const char *>(st.g);
+    bf16x8_t tg[2], tq[2];
+    tg[0] = tr_operand(gb, toff[0][0], toff[0][1], 0);
+    tq[0] = tr_operand(qb, toff[0][0], toff[0][1], 0);
 #pragma unroll
-    for (int st2 = 0; st2 < 2; ++st2) {
+    for (int j = 0; j < 8; ++j) {
+      const int st2 = j >> 2, db = j & 3;
+      if (j + 1 < 8) {
+        const int st2n = (j + 1) >> 2, dbn = (j + 1) & 3;
+        tg[(j + 1) & 1] = tr_operand(gb, toff[dbn][0], toff[dbn][1], st2n);
+        tq[(j + 1) & 1] = tr_operand(qb, toff[dbn][0], toff[dbn][1], st2n);
+      }
       const bf16x8_t pa = as_bf16x8(u32x4_t{pw[4 * st2], pw[4 * st2 + 1], pw[4 * st2 + 2], pw[4 * st2 + 3]});
       const bf16x8_t da = as_bf16x8(u32x4_t{dw[4 * st2], dw[4 * st2 + 1], dw[4 * st2 + 2], dw[4 * st2 + 3]});
-#pragma unroll
-      for (int db = 0; db < kD / 32; ++db) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, tr_operand(gb, toff[db][0], toff[db][1], st2),
-                                                         dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, tr_operand(qb, toff[db][0], toff[db][1], st2),
-                                                         dk[db], 0, 0, 0);
-      }
-    }
-    // Interleave: the look-ahead S/dP products (16 MFMA, 16 LDS reads) with this
-    // block's P/dS arithmetic, then the dV/dK products with their transposing reads.
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+      dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, tg[j & 1], dv[db], 0, 0, 0);
+      dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, tq[j & 1], dk[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
