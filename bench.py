@@ -13,7 +13,8 @@ Printed: one JSON line. `value` is decode tokens/s (B / step time). The
 K/V row once, plus q, out and the new k/v) against the 8 TB/s HBM peak.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 Secondary lines of the same JSON: the full-attention contrast (cache L_m + T)
-at a few decode lengths, and the packed 32K masked forward on matrix cores.
+at a few decode lengths, and the packed 32K masked forward (both prefix modes)
+and its backward on matrix cores.
 """
 from __future__ import annotations
 
@@ -260,13 +261,36 @@ def main():
         for mode, name in ((rs.RSWA_PREFIX_CAUSAL, "prefix_causal"), (rs.RSWA_PREFIX_FULL, "prefix_full")):
             run = lambda i: rs.rswa_masked_attn(Qd, Kd, Vd, Od, mw.seq_len, mw.ref_len, mw.window, mw.heads,
                                                 mw.head_dim, rs.RSWA_BF16, mode, 0.0, stream=stream)
-            run(0)
-            run(0)
-            ms_m = event_time_ms(run, 10, stream) / 10
+            for _ in range(5):
+                run(0)
+            ms_m = event_time_ms(run, 20, stream) / 20
             fl = masked_flops(mw.seq_len, mw.ref_len, mw.window, mw.heads, mw.head_dim,
                               mode == rs.RSWA_PREFIX_FULL)
             masked[name] = {"ms": ms_m, "algorithmic_flop": fl, "TFLOPs": fl / (ms_m * 1e-3) / 1e12,
                             "frac_of_bf16_peak": fl / (ms_m * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+        # packed 32K backward (dQ, dK, dV) of the causal-prefix forward
+        Gd = to_d(wl.packed_dout(mw))
+        lse = torch.empty((mw.heads, mw.seq_len), dtype=torch.float32, device="cuda")
+        rs.rswa_masked_attn(Qd, Kd, Vd, Od, mw.seq_len, mw.ref_len, mw.window, mw.heads, mw.head_dim,
+                            rs.RSWA_BF16, rs.RSWA_PREFIX_CAUSAL, 0.0, stream=stream, lse=lse)
+        ws_b = torch.empty(rs.rswa_masked_bwd_workspace_size(mw.seq_len, mw.ref_len, mw.heads),
+                           dtype=torch.uint8, device="cuda")
+        dq, dk, dv = torch.empty_like(Qd), torch.empty_like(Qd), torch.empty_like(Qd)
+        run_b = lambda i: rs.rswa_masked_attn_bwd(Qd, Kd, Vd, Od, Gd, lse, dq, dk, dv, mw.seq_len, mw.ref_len,
+                                                  mw.window, mw.heads, mw.head_dim, rs.RSWA_BF16,
+                                                  rs.RSWA_PREFIX_CAUSAL, 0.0, ws_b, stream=stream)
+        for _ in range(3):
+            run_b(0)
+        ms_b = event_time_ms(run_b, 10, stream) / 10
+        fl_b = 2.5 * masked_flops(mw.seq_len, mw.ref_len, mw.window, mw.heads, mw.head_dim, False)
+        masked["backward_prefix_causal"] = {
+            "ms": ms_b, "algorithmic_flop": fl_b, "TFLOPs": fl_b / (ms_b * 1e-3) / 1e12,
+            "frac_of_bf16_peak": fl_b / (ms_b * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "flop_convention": "2.5x the forward: five products of 2 d flop per visible pair (S, dP, dV, dK, "
+                               "dQ); the kernels execute seven (S and dP are formed in both the dQ and "
+                               "the dK/dV pass)",
+            "calls": "lse-producing forward excluded; pre-pass, dQ, dK/dV and reduction kernels included"}
+        del Gd, dq, dk, dv, ws_b
         result["masked_32k"] = {"workload": mw.name, "seq_len": mw.seq_len, "ref_len": mw.ref_len,
                                 "window": mw.window, "heads": mw.heads, **masked}
 
