@@ -14,7 +14,8 @@ K/V row once, plus q, out and the new k/v) against the 8 TB/s HBM peak.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 Secondary lines of the same JSON: the full-attention contrast (cache L_m + T)
 at a few decode lengths, and the packed 32K masked forward (both prefix modes)
-and its backward on matrix cores.
+and its backward, a multi-document 32K pack, and the prefill -> decode
+hand-off at the 40-page shape.
 """
 from __future__ import annotations
 
@@ -293,6 +294,61 @@ def main():
         del Gd, dq, dk, dv, ws_b
         result["masked_32k"] = {"workload": mw.name, "seq_len": mw.seq_len, "ref_len": mw.ref_len,
                                 "window": mw.window, "heads": mw.heads, **masked}
+
+        # several documents per 32K pack (samples independent), forward on matrix cores
+        cu, refs = wl.varlen_pack_layout(mw.seq_len, mw.base_seed)
+        lens = np.diff(cu)
+        cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
+        refs_d = torch.tensor(refs, dtype=torch.int32, device="cuda")
+        run_v = lambda i: rs.rswa_masked_attn_varlen(Qd, Kd, Vd, Od, cu_d, refs_d, len(refs), mw.seq_len,
+                                                     int(lens.max()), mw.window, mw.heads, mw.head_dim,
+                                                     rs.RSWA_BF16, rs.RSWA_PREFIX_CAUSAL, 0.0, stream=stream)
+        for _ in range(5):
+            run_v(0)
+        ms_v = event_time_ms(run_v, 20, stream) / 20
+        fl_v = sum(masked_flops(int(N_s), int(L_s), mw.window, mw.heads, mw.head_dim, False)
+                   for N_s, L_s in zip(lens, refs))
+        result["varlen_32k"] = {
+            "workload": "packed-32k-varlen-bf16", "samples": len(refs),
+            "sample_rows": [int(x) for x in lens], "ref_lens": [int(x) for x in refs],
+            "layout": "pages ~ U{2..16} (L = 256 pages + 32), outputs ~ U{256..2048}, filled front to back",
+            "ms": ms_v, "algorithmic_flop": fl_v, "TFLOPs": fl_v / (ms_v * 1e-3) / 1e12,
+            "frac_of_bf16_peak": fl_v / (ms_v * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+        del Qd, Kd, Vd, Od, cu_d, refs_d
+
+        # prefill -> decode hand-off at the 40-page decode shape: B sequences of L_m reference
+        # rows plus T0 = n outputs (the window full at hand-off), one call for the whole batch
+        T0 = n
+        rows_b = L + T0
+        total = B * rows_b
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(w.base_seed)
+        pq, pk, pv = (torch.randn((total, H, d), device="cuda", generator=gen).to(torch.bfloat16)
+                      for _ in range(3))
+        pout = torch.empty_like(pq)
+        pcu = torch.arange(0, total + 1, rows_b, dtype=torch.int32, device="cuda")
+        pcache = rs.KVCache.allocate([L] * B, H, d, n, dtype=rs.RSWA_BF16)
+        run_p = lambda i: rs.rswa_prefill(pcache.desc, pq, pk, pv, pout, pcu, total, rows_b,
+                                          rs.RSWA_PREFIX_CAUSAL, 0.0, stream=stream)
+        prefs = torch.full((B,), L, dtype=torch.int32, device="cuda")
+        run_pf = lambda i: rs.rswa_masked_attn_varlen(pq, pk, pv, pout, pcu, prefs, B, total, rows_b, n, H, d,
+                                                      rs.RSWA_BF16, rs.RSWA_PREFIX_CAUSAL, 0.0, stream=stream)
+        for _ in range(2):
+            run_p(0)
+        ms_p = event_time_ms(run_p, 5, stream) / 5
+        ms_pf = event_time_ms(run_pf, 5, stream) / 5
+        if rs.rswa_check_device_error(pcache.desc):
+            print("prefill reported device errors", file=sys.stderr)
+            sys.exit(1)
+        fl_p = B * masked_flops(rows_b, L, n, H, d, False)
+        copy_bytes = 2 * 2 * B * H * (L + min(n, T0)) * d * 2  # K and V rows, read + write
+        result["prefill_40page"] = {
+            "workload": "40-page-prefill-bf16", "batch": B, "ref_len": L, "outputs_T0": T0,
+            "rows": total, "ms": ms_p, "forward_only_ms": ms_pf,
+            "forward_algorithmic_flop": fl_p, "forward_TFLOPs": fl_p / (ms_pf * 1e-3) / 1e12,
+            "handoff_bytes": copy_bytes,
+            "handoff_GBps_from_difference": copy_bytes / max(1e-9, (ms_p - ms_pf) * 1e-3) / 1e9}
+        del pq, pk, pv, pout, pcache
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, kref, vref, W + K, args.cpu_seconds)

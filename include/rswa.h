@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RSWA_ABI_VERSION 2
+#define RSWA_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define RSWA_API __attribute__((visibility("default")))
@@ -73,6 +73,8 @@ typedef enum { RSWA_PREFIX_CAUSAL = 0, RSWA_PREFIX_FULL = 1 } rswa_prefix_mode_t
 #define RSWA_DEVERR_STEP 2      /* step[b] < 0, or step[b] would overflow int32      */
 #define RSWA_DEVERR_EMPTY 4     /* decode with nothing visible (L_m = 0 and T = 0)   */
 #define RSWA_DEVERR_ALIGN 8     /* seq_base[b] / ref_base[b] not 16-byte aligned     */
+#define RSWA_DEVERR_PACK 16     /* prefill: cu_seqlens inconsistent for sequence b,
+                                   or ref_len[b] larger than its rows                */
 
 /*
  * KV cache descriptor (plain struct, caller-owned, passed by pointer).
@@ -183,6 +185,53 @@ RSWA_API rswa_status_t rswa_masked_attn(const void *q, const void *k, const void
                                float *lse, int32_t seq_len, int32_t ref_len, int32_t window,
                                int32_t num_heads, int32_t head_dim, int32_t dtype,
                                int32_t prefix_mode, float scale, void *stream);
+
+/*
+ * Packed forward over several samples per pack ("varlen"): sample s owns rows
+ * [cu_seqlens[s], cu_seqlens[s+1]) of q, k, v, out (same [rows][H][head_dim]
+ * bf16 layout as rswa_masked_attn, total_tokens rows in all) and has its own
+ * reference length ref_lens[s]; inside a sample the visibility is exactly that
+ * of rswa_masked_attn, and no row sees another sample's keys. The pages pack
+ * 2-50-page samples into 32K sequences for training (WeThinkIn page, section
+ * 实验与证据.1) without stating a cross-sample mask; this call takes the reading
+ * that samples are independent.
+ *  cu_seqlens   device int32 [num_seqs + 1], non-decreasing, cu_seqlens[0] >= 0,
+ *               cu_seqlens[num_seqs] <= total_tokens.
+ *  ref_lens     device int32 [num_seqs], 0 <= ref_lens[s] <= sample length.
+ *  max_seq_len  host bound on every sample's length (sets the grid).
+ *  lse          NULL, or device float [num_heads][total_tokens] (per pack row).
+ * The device arrays are not read on the host: a sample that breaks these
+ * rules (or is longer than max_seq_len) is skipped and its rows are not
+ * written. Rows outside every sample are not written either.
+ */
+RSWA_API rswa_status_t rswa_masked_attn_varlen(const void *q, const void *k, const void *v, void *out,
+                                      float *lse, const int32_t *cu_seqlens,
+                                      const int32_t *ref_lens, int32_t num_seqs,
+                                      int32_t total_tokens, int32_t max_seq_len, int32_t window,
+                                      int32_t num_heads, int32_t head_dim, int32_t dtype,
+                                      int32_t prefix_mode, float scale, void *stream);
+
+/*
+ * Prefill -> decode hand-off for every sequence of a cache: sample b of the
+ * pack (rows [cu_seqlens[b], cu_seqlens[b+1]), cu_seqlens device int32
+ * [batch + 1]) is sequence b's reference segment (ref_len[b] rows, the
+ * cache's device value) followed by its first T0_b = rows - ref_len[b]
+ * outputs (output t at row ref_len[b] + t - 1, the token whose query is q_t).
+ * One call runs the packed forward of every sample (as rswa_masked_attn_varlen
+ * with window = cache->window, out and lse as there) and leaves the cache as
+ * rswa_cache_init followed by T0_b appends would: reference rows in slots
+ * 0 .. ref_len[b]-1, the last min(window, T0_b) outputs in their ring slots
+ * ref_len[b] + ((t-1) mod window), step[b] = T0_b (yhxrc and 夜雨聆风 pages;
+ * WeThinkIn page, Eq. (6)). Decode then continues with output T0_b + 1.
+ *  q, k, v, out  device [total_tokens][num_heads][head_dim], cache dtype; only
+ *                RSWA_BF16 with head_dim 128 (the packed kernel's case).
+ * A sequence whose metadata are invalid gets RSWA_DEVERR_PACK (or the cache's
+ * usual bits) in the error word and is left untouched; the forward skips it.
+ */
+RSWA_API rswa_status_t rswa_prefill(const rswa_cache_t *cache, const void *q, const void *k,
+                           const void *v, void *out, float *lse, const int32_t *cu_seqlens,
+                           int32_t total_tokens, int32_t max_seq_len, int32_t prefix_mode,
+                           float scale, void *stream);
 
 /*
  * Bytes of device workspace rswa_masked_attn_bwd needs for these sizes and

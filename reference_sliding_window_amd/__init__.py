@@ -39,10 +39,12 @@ RSWA_DEVERR_REF_LEN = 1
 RSWA_DEVERR_STEP = 2
 RSWA_DEVERR_EMPTY = 4
 RSWA_DEVERR_ALIGN = 8
+RSWA_DEVERR_PACK = 16
 
 EXPORTED = ("rswa_abi_version", "rswa_status_str", "rswa_cache_init", "rswa_append_kv",
             "rswa_decode_workspace_size", "rswa_decode_attn", "rswa_masked_attn",
-            "rswa_masked_bwd_workspace_size", "rswa_masked_attn_bwd", "rswa_check_device_error")
+            "rswa_masked_attn_varlen", "rswa_prefill", "rswa_masked_bwd_workspace_size",
+            "rswa_masked_attn_bwd", "rswa_check_device_error")
 
 
 class RswaError(RuntimeError):
@@ -88,6 +90,9 @@ def _lib() -> ctypes.CDLL:
             "rswa_decode_workspace_size": (SZ, [D, I32]),
             "rswa_decode_attn": (I32, [D, P, P, P, P, F, I32, P, SZ, P]),
             "rswa_masked_attn": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, P]),
+            "rswa_masked_attn_varlen": (I32, [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
+                                              I32, F, P]),
+            "rswa_prefill": (I32, [D, P, P, P, P, P, P, I32, I32, I32, F, P]),
             "rswa_masked_bwd_workspace_size": (SZ, [I32, I32, I32, I32]),
             "rswa_masked_attn_bwd": (I32, [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
                                            I32, F, I32, P, SZ, P]),
@@ -175,6 +180,26 @@ def rswa_masked_attn(q, k, v, out, seq_len: int, ref_len: int, window: int, num_
                                  window, num_heads, head_dim, dtype, prefix_mode, float(scale),
                                  _stream(stream))
     return _check(st, "rswa_masked_attn") if check else st
+
+
+def rswa_masked_attn_varlen(q, k, v, out, cu_seqlens, ref_lens, num_seqs: int, total_tokens: int,
+                            max_seq_len: int, window: int, num_heads: int, head_dim: int,
+                            dtype: int = RSWA_BF16, prefix_mode: int = RSWA_PREFIX_CAUSAL,
+                            scale: float = 0.0, stream=None, check=True, lse=None) -> int:
+    st = _lib().rswa_masked_attn_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens),
+                                        _ptr(ref_lens), num_seqs, total_tokens, max_seq_len, window,
+                                        num_heads, head_dim, dtype, prefix_mode, float(scale),
+                                        _stream(stream))
+    return _check(st, "rswa_masked_attn_varlen") if check else st
+
+
+def rswa_prefill(desc: CacheDesc, q, k, v, out, cu_seqlens, total_tokens: int, max_seq_len: int,
+                 prefix_mode: int = RSWA_PREFIX_CAUSAL, scale: float = 0.0, stream=None, check=True,
+                 lse=None) -> int:
+    st = _lib().rswa_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                             _ptr(cu_seqlens), total_tokens, max_seq_len, prefix_mode, float(scale),
+                             _stream(stream))
+    return _check(st, "rswa_prefill") if check else st
 
 
 def rswa_masked_bwd_workspace_size(seq_len: int, ref_len: int, num_heads: int,

@@ -248,6 +248,8 @@ rswa_status_t rswa_masked_attn(const void *q, const void *k, const void *v, void
   p.v = v;
   p.out = out;
   p.lse = lse;
+  p.num_seqs = 1;
+  p.max_seq_len = seq_len;
   p.seq_len = seq_len;
   p.ref_len = ref_len;
   p.window = window;
@@ -256,6 +258,93 @@ rswa_status_t rswa_masked_attn(const void *q, const void *k, const void *v, void
   const float sc = scale == 0.f ? 1.f / sqrtf((float)head_dim) : scale;
   p.scale_log2 = sc * kLog2e;
   const hipError_t e = launch_masked(p, head_dim, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
+}
+
+rswa_status_t rswa_masked_attn_varlen(const void *q, const void *k, const void *v, void *out,
+                                      float *lse, const int32_t *cu_seqlens,
+                                      const int32_t *ref_lens, int32_t num_seqs,
+                                      int32_t total_tokens, int32_t max_seq_len, int32_t window,
+                                      int32_t num_heads, int32_t head_dim, int32_t dtype,
+                                      int32_t prefix_mode, float scale, void *stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || cu_seqlens == nullptr ||
+      ref_lens == nullptr)
+    return RSWA_ERR_NULL;
+  if (num_seqs < 0 || total_tokens < 0 || max_seq_len < 0 || window < 1 || num_heads < 1)
+    return RSWA_ERR_SHAPE;
+  if (dtype != RSWA_BF16 || head_dim != 128) return RSWA_ERR_UNSUPPORTED;
+  if (prefix_mode != RSWA_PREFIX_CAUSAL && prefix_mode != RSWA_PREFIX_FULL)
+    return RSWA_ERR_UNSUPPORTED;
+  if ((int64_t)total_tokens * num_heads * head_dim >= ((int64_t)1 << 31)) return RSWA_ERR_CAPACITY;
+  if ((int64_t)num_seqs * num_heads * ((max_seq_len + 127) / 128) >= ((int64_t)1 << 31))
+    return RSWA_ERR_CAPACITY;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RSWA_ERR_ALIGN;
+  if (((reinterpret_cast<uintptr_t>(cu_seqlens) | reinterpret_cast<uintptr_t>(ref_lens)) & 3u) != 0)
+    return RSWA_ERR_ALIGN;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RSWA_ERR_ALIGN;
+  if (!isfinite(scale)) return RSWA_ERR_SHAPE;
+  if (num_seqs == 0 || total_tokens == 0 || max_seq_len == 0) return RSWA_OK;
+  MaskedParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.cu_seqlens = cu_seqlens;
+  p.ref_lens = ref_lens;
+  p.num_seqs = num_seqs;
+  p.max_seq_len = max_seq_len;
+  p.seq_len = total_tokens;
+  p.window = window;
+  p.heads = num_heads;
+  p.prefix_mode = prefix_mode;
+  const float sc = scale == 0.f ? 1.f / sqrtf((float)head_dim) : scale;
+  p.scale_log2 = sc * kLog2e;
+  const hipError_t e = launch_masked(p, head_dim, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
+}
+
+rswa_status_t rswa_prefill(const rswa_cache_t *cache, const void *q, const void *k, const void *v,
+                           void *out, float *lse, const int32_t *cu_seqlens, int32_t total_tokens,
+                           int32_t max_seq_len, int32_t prefix_mode, float scale, void *stream) {
+  const rswa_status_t st = check_cache(cache);
+  if (st != RSWA_OK) return st;
+  if (cache->dtype != RSWA_BF16 || cache->head_dim != 128) return RSWA_ERR_UNSUPPORTED;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || cu_seqlens == nullptr)
+    return RSWA_ERR_NULL;
+  if (total_tokens < 0 || max_seq_len < 0) return RSWA_ERR_SHAPE;
+  if (prefix_mode != RSWA_PREFIX_CAUSAL && prefix_mode != RSWA_PREFIX_FULL)
+    return RSWA_ERR_UNSUPPORTED;
+  if ((int64_t)total_tokens * cache->num_heads * cache->head_dim >= ((int64_t)1 << 31))
+    return RSWA_ERR_CAPACITY;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RSWA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return RSWA_ERR_ALIGN;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RSWA_ERR_ALIGN;
+  if (!isfinite(scale)) return RSWA_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (total_tokens > 0 && max_seq_len > 0) {
+    const rswa_status_t fs = rswa_masked_attn_varlen(
+        q, k, v, out, lse, cu_seqlens, cache->ref_len, cache->batch, total_tokens, max_seq_len,
+        cache->window, cache->num_heads, cache->head_dim, cache->dtype, prefix_mode, scale, stream);
+    if (fs != RSWA_OK) return fs;
+  }
+  HandoffParams hp{};
+  hp.k_src = k;
+  hp.v_src = v;
+  hp.cu_seqlens = cu_seqlens;
+  hp.k = cache->k;
+  hp.v = cache->v;
+  hp.seq_base = cache->seq_base;
+  hp.ref_len = cache->ref_len;
+  hp.step = cache->step;
+  hp.error = cache->error;
+  hp.batch = cache->batch;
+  hp.heads = cache->num_heads;
+  hp.window = cache->window;
+  hp.max_ref_len = cache->max_ref_len;
+  hp.total_tokens = total_tokens;
+  hp.max_seq_len = max_seq_len;
+  const hipError_t e = launch_handoff(hp, cache->dtype, cache->head_dim, s);
   return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
 }
 

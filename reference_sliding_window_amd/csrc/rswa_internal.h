@@ -79,9 +79,30 @@ struct MaskedParams {
   const void *k;
   const void *v;
   void *out;
-  float *lse;  // nullable [H][N], natural log of each row's softmax normaliser
-  int32_t seq_len, ref_len, window, heads, prefix_mode;
+  float *lse;  // nullable [H][seq_len], natural log of each row's softmax normaliser
+  // Several samples per pack: cu_seqlens (device [num_seqs + 1]) and ref_lens
+  // (device [num_seqs]); nullptr for one sequence of seq_len rows and ref_len.
+  const int32_t *cu_seqlens;
+  const int32_t *ref_lens;
+  int32_t num_seqs, max_seq_len;
+  int32_t seq_len, ref_len, window, heads, prefix_mode;  // seq_len: total rows of the pack
   float scale_log2;
+};
+
+// Writes a prefilled pack into the cache: per sequence b (sample b of the pack),
+// the reference rows and the last min(n, T0) output rows into their slots, and
+// step[b] = T0 = rows - ref_len[b].
+struct HandoffParams {
+  const void *k_src;
+  const void *v_src;
+  const int32_t *cu_seqlens;
+  void *k;
+  void *v;
+  const int64_t *seq_base;
+  const int32_t *ref_len;
+  int32_t *step;
+  int32_t *error;
+  int32_t batch, heads, window, max_ref_len, total_tokens, max_seq_len;
 };
 
 struct MaskedBwdParams {
@@ -121,5 +142,6 @@ struct BwdPlan {
 BwdPlan plan_masked_bwd(int32_t seq_len, int32_t ref_len, int32_t heads, int32_t requested_parts);
 hipError_t launch_masked_bwd(const MaskedBwdParams &p, hipStream_t s);
 hipError_t launch_clear_word(int32_t *word, hipStream_t s);
+hipError_t launch_handoff(const HandoffParams &p, int32_t dtype, int32_t head_dim, hipStream_t s);
 
 }  // namespace rswa

@@ -73,24 +73,39 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
 
 __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParams p) {
   __shared__ Tile k_sm[2], v_sm[2];
-  const int N = p.seq_len, H = p.heads, Lm = p.ref_len, n = p.window;
+  const int H = p.heads, n = p.window;
   const bool full_prefix = p.prefix_mode == RSWA_PREFIX_FULL;
-  const int nqb = (N + kBM - 1) / kBM;
-  const int G = nqb * H;
-  // XCD-aware order: logical work item w -> (head, query block)
+  const int nqb = (p.max_seq_len + kBM - 1) / kBM;
+  const int G = p.num_seqs * H * nqb;
+  // XCD-aware order: logical work item w -> (sample, head, query block), so that
+  // the query blocks of one (sample, head) share an XCD and its L2.
   int w = blockIdx.x;
   if ((G & 7) == 0) w = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  const int h = w / nqb;
+  const int sample = w / (H * nqb);
+  const int h = (w / nqb) % H;
   const int q0 = (w % nqb) * kBM;
+  // One sample of the pack: rows [row0, row0 + N) with its own reference
+  // length; no row sees another sample's keys.
+  int row0 = 0, N = p.seq_len, Lm = p.ref_len;
+  if (p.cu_seqlens != nullptr) {
+    row0 = p.cu_seqlens[sample];
+    const int row1 = p.cu_seqlens[sample + 1];
+    Lm = p.ref_lens[sample];
+    N = row1 - row0;
+    // device-side metadata: a malformed sample is skipped
+    if (row0 < 0 || row1 < row0 || row1 > p.seq_len || N > p.max_seq_len || Lm < 0 || Lm > N) return;
+  }
+  if (q0 >= N) return;
   const int q_end = min(N, q0 + kBM);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi = lane >> 5, l32 = lane & 31;
   const uint32_t stride = (uint32_t)H * kD;
-  const uint16_t *Qg = static_cast<const uint16_t *>(p.q) + (int64_t)h * kD;
-  const uint16_t *Kg = static_cast<const uint16_t *>(p.k) + (int64_t)h * kD;
-  const uint16_t *Vg = static_cast<const uint16_t *>(p.v) + (int64_t)h * kD;
-  uint16_t *Og = static_cast<uint16_t *>(p.out) + (int64_t)h * kD;
+  const int64_t base = (int64_t)row0 * stride + (int64_t)h * kD;
+  const uint16_t *Qg = static_cast<const uint16_t *>(p.q) + base;
+  const uint16_t *Kg = static_cast<const uint16_t *>(p.k) + base;
+  const uint16_t *Vg = static_cast<const uint16_t *>(p.v) + base;
+  uint16_t *Og = static_cast<uint16_t *>(p.out) + base;
 
   // Key blocks: the reference segment [0, pre_hi), then the output keys
   // [win_lo, win_hi) some row of this workgroup sees.
@@ -270,7 +285,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
   if (!q_ok) return;
   const float inv = 1.f / l;
   if (p.lse != nullptr && hi == 0)  // natural log of sum_j 2^(c s_j) = (c m + log2 l) ln 2
-    p.lse[(int64_t)h * N + qi] = (m * c + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
+    p.lse[(int64_t)h * p.seq_len + row0 + qi] = (m * c + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
   uint16_t *orow = Og + (int64_t)qi * stride;
 #pragma unroll
   for (int db = 0; db < kD / 32; ++db) {
@@ -288,8 +303,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
 
 hipError_t launch_masked(const MaskedParams &p, int32_t head_dim, hipStream_t s) {
   if (head_dim != kD) return hipErrorInvalidValue;
-  const int nqb = (p.seq_len + kBM - 1) / kBM;
-  const int64_t G = (int64_t)nqb * p.heads;
+  const int nqb = (p.max_seq_len + kBM - 1) / kBM;
+  const int64_t G = (int64_t)nqb * p.heads * p.num_seqs;
+  if (G == 0) return hipSuccess;
   hipLaunchKernelGGL(masked_attn_kernel, dim3((unsigned)G), dim3(64 * kWaves), 0, s, p);
   return hipGetLastError();
 }

@@ -133,6 +133,49 @@ def test_masked_argument_checks():
     assert m(seq_len=0, ref_len=0) == rs.RSWA_OK   # nothing to do, nothing enqueued
 
 
+def test_varlen_argument_checks():
+    base = dict(q=A, k=A, v=A, out=A, cu_seqlens=A, ref_lens=A + 64, num_seqs=3, total_tokens=900,
+                max_seq_len=400, window=8, num_heads=2, head_dim=128)
+    m = lambda **kw: rs.rswa_masked_attn_varlen(**{**base, **kw}, check=False)
+    for name in ("q", "k", "v", "out", "cu_seqlens", "ref_lens"):
+        assert m(**{name: None}) == rs.RSWA_ERR_NULL, name
+    assert m(num_seqs=-1) == rs.RSWA_ERR_SHAPE
+    assert m(total_tokens=-1) == rs.RSWA_ERR_SHAPE
+    assert m(max_seq_len=-1) == rs.RSWA_ERR_SHAPE
+    assert m(window=0) == rs.RSWA_ERR_SHAPE
+    assert m(num_heads=0) == rs.RSWA_ERR_SHAPE
+    assert m(head_dim=64) == rs.RSWA_ERR_UNSUPPORTED
+    assert m(dtype=rs.RSWA_FP32) == rs.RSWA_ERR_UNSUPPORTED
+    assert m(prefix_mode=9) == rs.RSWA_ERR_UNSUPPORTED
+    assert m(total_tokens=2 ** 20, num_heads=16) == rs.RSWA_ERR_CAPACITY
+    assert m(q=A + 8) == rs.RSWA_ERR_ALIGN
+    assert m(cu_seqlens=A + 2) == rs.RSWA_ERR_ALIGN
+    assert m(lse=A + 1) == rs.RSWA_ERR_ALIGN
+    assert m(scale=math.nan) == rs.RSWA_ERR_SHAPE
+    assert m(num_seqs=0) == rs.RSWA_OK            # nothing to do, nothing enqueued
+    assert m(total_tokens=0) == rs.RSWA_OK
+    assert m(max_seq_len=0) == rs.RSWA_OK
+
+
+def test_prefill_argument_checks():
+    desc = good_desc()
+    p = lambda **kw: rs.rswa_prefill(**{**dict(desc=desc, q=A, k=A, v=A, out=A, cu_seqlens=A, total_tokens=500,
+                                              max_seq_len=300), **kw}, check=False)
+    for name in ("q", "k", "v", "out", "cu_seqlens"):
+        assert p(**{name: None}) == rs.RSWA_ERR_NULL, name
+    assert p(desc=good_desc(head_dim=64)) == rs.RSWA_ERR_UNSUPPORTED
+    assert p(desc=good_desc(dtype=rs.RSWA_FP32)) == rs.RSWA_ERR_UNSUPPORTED
+    assert p(desc=good_desc(k=None)) == rs.RSWA_ERR_NULL
+    assert p(desc=good_desc(batch=0)) == rs.RSWA_ERR_SHAPE
+    assert p(total_tokens=-1) == rs.RSWA_ERR_SHAPE
+    assert p(max_seq_len=-3) == rs.RSWA_ERR_SHAPE
+    assert p(prefix_mode=5) == rs.RSWA_ERR_UNSUPPORTED
+    assert p(total_tokens=2 ** 22) == rs.RSWA_ERR_CAPACITY
+    assert p(out=A + 4) == rs.RSWA_ERR_ALIGN
+    assert p(cu_seqlens=A + 1) == rs.RSWA_ERR_ALIGN
+    assert p(scale=math.inf) == rs.RSWA_ERR_SHAPE
+
+
 def test_masked_bwd_workspace_size():
     ws = rs.rswa_masked_bwd_workspace_size
     assert ws(-1, 0, 2) == 0

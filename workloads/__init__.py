@@ -30,7 +30,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 # tensor ids used in seed words
-TID_Q, TID_K, TID_V, TID_KREF, TID_VREF, TID_RAGGED, TID_DOUT = 0, 1, 2, 3, 4, 5, 6
+TID_Q, TID_K, TID_V, TID_KREF, TID_VREF, TID_RAGGED, TID_DOUT, TID_PACK = 0, 1, 2, 3, 4, 5, 6, 7
 
 PAGE_TOKENS = 256   # vision tokens per 1024x1024 page
 PROMPT_TOKENS = 32  # prompt length (not stated on the pages; fixed here)
@@ -202,6 +202,32 @@ def packed_dout(w: MaskedWorkload, sigma: float = 1.0):
     """Upstream gradient dO of the packed forward's output, [N][H][d] in storage
     form, N(0, sigma^2) (the loss is sum(dO * O))."""
     return draw(w.dtype, sigma, (w.seq_len, w.heads, w.head_dim), w.base_seed, TID_DOUT)
+
+
+def varlen_pack_layout(total_tokens: int, base_seed: int, pages=(2, 16), outputs=(256, 2048),
+                       page_tokens: int = 256, prompt_tokens: int = 32):
+    """Sample boundaries of a pack of several documents, filled front to back.
+
+    Each sample is a reference segment of L = page_tokens * pages + prompt_tokens
+    (pages ~ U{pages}) followed by T ~ U{outputs} output tokens. When the next
+    sample does not fit, it is shrunk to the rows left (fewer pages, then fewer
+    outputs, at least one output); rows too few for a two-page sample stay
+    outside every sample. Returns (cu_seqlens [S+1], ref_lens [S]) as int32.
+    """
+    g = _rng(base_seed, TID_PACK)
+    cu, refs, used = [0], [], 0
+    min_len = page_tokens * pages[0] + prompt_tokens + 1
+    while total_tokens - used >= min_len:
+        left = total_tokens - used
+        p = int(g.integers(pages[0], pages[1] + 1))
+        t = int(g.integers(outputs[0], outputs[1] + 1))
+        p = min(p, (left - prompt_tokens - 1) // page_tokens)
+        L = page_tokens * p + prompt_tokens
+        t = min(t, left - L)
+        used += L + t
+        cu.append(used)
+        refs.append(L)
+    return np.asarray(cu, np.int32), np.asarray(refs, np.int32)
 
 
 # --------------------------------------------------------------------------- ragged
