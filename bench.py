@@ -14,8 +14,9 @@ K/V row once, plus q, out and the new k/v) against the 8 TB/s HBM peak.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 Secondary lines of the same JSON: the full-attention contrast (cache L_m + T)
 at a few decode lengths, and the packed 32K masked forward (both prefix modes)
-and its backward, a multi-document 32K pack, and the prefill -> decode
-hand-off at the 40-page shape.
+and its backward, a multi-document 32K pack, the prefill -> decode hand-off
+at the 40-page shape, and a multi-layer decode step replayed as one HIP graph
+at the output lengths of the pages' TPS table (R-SWA against full attention).
 """
 from __future__ import annotations
 
@@ -133,6 +134,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the contrast and masked lines")
+    ap.add_argument("--layers", type=int, default=12,
+                    help="attention layers in the multi-layer graph line (the pages do not state the count)")
     ap.add_argument("--copy-reference", action="store_true",
                     help="first run a plain 1 GiB device copy 3 times (scale reference for HBM counters)")
     args = ap.parse_args()
@@ -228,30 +231,30 @@ def main():
     del qs, ks, vs
 
     if not args.no_secondary:
-        # full-attention contrast: the same kernels with a window >= every output (cache L_m + T)
-        Tmax = w.steps
-        con = rs.KVCache.allocate([L] * B, H, d, Tmax, dtype=rs.RSWA_BF16)
-        con.k.normal_(0.0, w.sigma_kv)
-        con.v.normal_(0.0, w.sigma_kv)
-        cws = con.workspace()
+        # full-attention contrast: the same kernels over a cache of exactly L_m + T slots (window T,
+        # every output kept), attend-only at output T
         q1 = torch.randn((B, H, d), device="cuda").to(torch.bfloat16)
         contrast = {}
         for T in (256, 2048, 4096, 6144):
-            con.step.fill_(T)   # attend-only call over the L_m + T cached slots
+            con = rs.KVCache.allocate([L] * B, H, d, T, dtype=rs.RSWA_BF16)
+            con.k.normal_(0.0, w.sigma_kv)
+            con.v.normal_(0.0, w.sigma_kv)
+            con.step.fill_(T)
+            cws = con.workspace()
             ms_c = event_time_ms(lambda i: rs.rswa_decode_attn(con.desc, q1, out, None, None, 0.0, 0, cws,
                                                              stream=stream), 20, stream) / 20
             contrast[str(T)] = {"ms_per_step": ms_c, "cache_slots": L + T,
-                                "GBps": decode_bytes(B, H, d, L, Tmax, T) / (ms_c * 1e-3) / 1e9}
+                                "GBps": decode_bytes(B, H, d, L, T, T) / (ms_c * 1e-3) / 1e9}
+            del con, cws
         # the R-SWA cache at the same attend-only call, for a like-for-like comparison
         ms_r = event_time_ms(lambda i: rs.rswa_decode_attn(cache.desc, q1, out, None, None, 0.0, 0, ws,
                                                          stream=stream), 20, stream) / 20
         result["contrast_full_attention"] = {
-            "what": "attend-only decode call; full attention keeps L_m + T slots (window >= all outputs), "
-                    "R-SWA keeps L_m + 128",
+            "what": "attend-only decode call; full attention keeps L_m + T slots (a cache of exactly that "
+                    "size, window = T), R-SWA keeps L_m + 128",
             "full_attention_per_T": contrast,
             "rswa_attend_only_ms": ms_r,
             "rswa_fused_step_ms": ms_per_step}
-        del con
         # packed 32K masked forward (matrix cores)
         mw = wl.PACKED_32K
         Q, Kp, Vp = wl.packed_qkv(mw)
@@ -349,6 +352,65 @@ def main():
             "handoff_bytes": copy_bytes,
             "handoff_GBps_from_difference": copy_bytes / max(1e-9, (ms_p - ms_pf) * 1e-3) / 1e9}
         del pq, pk, pv, pout, pcache
+
+        # a decode step through `layers` attention layers (own cache each) as one HIP graph, at the
+        # output lengths of the pages' TPS table, R-SWA against full attention (attention share only)
+        layers = args.layers
+        r_caches = [rs.KVCache.allocate([L] * B, H, d, n, dtype=rs.RSWA_BF16) for _ in range(layers)]
+        for c in r_caches:
+            c.k.normal_(0.0, w.sigma_kv)
+            c.v.normal_(0.0, w.sigma_kv)
+        gq = [torch.randn((B, H, d), device="cuda").to(torch.bfloat16) for _ in range(layers)]
+        gk = [torch.randn((B, H, d), device="cuda").to(torch.bfloat16) for _ in range(layers)]
+        gv = [torch.randn((B, H, d), device="cuda").to(torch.bfloat16) for _ in range(layers)]
+        gout = [torch.empty_like(x) for x in gq]
+        ws_r = r_caches[0].workspace()
+        _, g_r = rs.rswa_decode_graph_create([c.desc for c in r_caches], gq, gout, workspace=ws_r)
+        _, g_rf = rs.rswa_decode_graph_create([c.desc for c in r_caches], gq, gout, gk, gv, workspace=ws_r)
+        per_T = {}
+        try:
+            for T in (256, 2048, 4096, 6144):
+                # full attention: per layer a cache of exactly L_m + T slots
+                f_caches = [rs.KVCache.allocate([L] * B, H, d, T, dtype=rs.RSWA_BF16) for _ in range(layers)]
+                for c in f_caches:
+                    c.k.normal_(0.0, w.sigma_kv)
+                    c.v.normal_(0.0, w.sigma_kv)
+                    c.step.fill_(T)
+                for c in r_caches:
+                    c.step.fill_(T)
+                ws_f = f_caches[0].workspace()
+                _, g_f = rs.rswa_decode_graph_create([c.desc for c in f_caches], gq, gout, workspace=ws_f)
+                try:
+                    rs.rswa_decode_graph_launch(g_r, stream=stream)
+                    rs.rswa_decode_graph_launch(g_f, stream=stream)
+                    ms_gr = event_time_ms(lambda i: rs.rswa_decode_graph_launch(g_r, stream=stream), 10,
+                                          stream) / 10
+                    ms_gf = event_time_ms(lambda i: rs.rswa_decode_graph_launch(g_f, stream=stream), 10,
+                                          stream) / 10
+                finally:
+                    rs.rswa_decode_graph_destroy(g_f)
+                per_T[str(T)] = {"rswa_ms_per_step": ms_gr, "full_ms_per_step": ms_gf,
+                                 "rswa_tokens_per_s": B / (ms_gr * 1e-3), "full_tokens_per_s": B / (ms_gf * 1e-3),
+                                 "rswa_over_full": ms_gf / ms_gr}
+                del f_caches, ws_f
+            for c in r_caches:
+                c.step.fill_(w.steps)
+            rs.rswa_decode_graph_launch(g_rf, stream=stream)
+            ms_rf = event_time_ms(lambda i: rs.rswa_decode_graph_launch(g_rf, stream=stream), 10, stream) / 10
+            for c in r_caches:
+                if rs.rswa_check_device_error(c.desc):
+                    print("multi-layer decode reported device errors", file=sys.stderr)
+                    sys.exit(1)
+        finally:
+            for g in (g_r, g_rf):
+                rs.rswa_decode_graph_destroy(g)
+        result["multi_layer_graph"] = {
+            "what": "one decode step through `layers` attention layers replayed as one HIP graph "
+                    "(rswa_decode_graph_*); attend-only at fixed T for both cache kinds; the pages' TPS "
+                    "table covers the whole model, this is its attention share",
+            "layers": layers, "batch": B, "ref_len": L, "window": n, "per_T": per_T,
+            "rswa_fused_step_ms": ms_rf, "rswa_fused_tokens_per_s": B / (ms_rf * 1e-3)}
+        del r_caches, ws_r, gq, gk, gv, gout
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, kref, vref, W + K, args.cpu_seconds)

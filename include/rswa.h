@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RSWA_ABI_VERSION 3
+#define RSWA_ABI_VERSION 4
 
 #if defined(__GNUC__)
 #define RSWA_API __attribute__((visibility("default")))
@@ -274,6 +274,39 @@ RSWA_API rswa_status_t rswa_masked_attn_bwd(const void *q, const void *k, const 
                                    int32_t head_dim, int32_t dtype, int32_t prefix_mode,
                                    float scale, int32_t num_parts, void *workspace,
                                    size_t workspace_bytes, void *stream);
+
+/*
+ * A decode step through several attention layers as one HIP graph. A decoder
+ * replaces every attention layer with R-SWA (WeThinkIn page, 核心导读), so a
+ * decode step is one rswa_decode_attn per layer, each with its own cache. These
+ * calls record the num_layers calls once -- layer l:
+ *   rswa_decode_attn(&caches[l], q[l], out[l], k_new ? k_new[l] : NULL,
+ *                    v_new ? v_new[l] : NULL, scale, num_splits, workspace, ...)
+ * in that order -- and replay them with one launch. The arrays are host arrays
+ * read at creation; the device buffers they name are baked into the graph, so
+ * a caller refreshes q/k_new/v_new in place between launches. Each replay runs
+ * exactly what the eager calls would (same kernels, same step counters on the
+ * device: fused calls advance step[b] on every replay). One workspace serves
+ * every layer (the layers run in order); it must hold
+ * max over l of rswa_decode_workspace_size(&caches[l], num_splits).
+ *  create   validates every layer as rswa_decode_attn would (nothing is
+ *           enqueued on failure), captures on an internal stream and
+ *           instantiates; *graph receives an opaque handle (host memory plus
+ *           HIP graph objects, freed by rswa_decode_graph_destroy).
+ *  launch   enqueues one replay on `stream` (asynchronous).
+ * The captured work holds no memset nodes, only the decode kernels. Replays
+ * of one graph, and replays of graphs that share caches or workspace, must
+ * not run concurrently.
+ */
+typedef struct rswa_decode_graph rswa_decode_graph_t;
+
+RSWA_API rswa_status_t rswa_decode_graph_create(const rswa_cache_t *caches, int32_t num_layers,
+                                       const void *const *q, void *const *out,
+                                       const void *const *k_new, const void *const *v_new,
+                                       float scale, int32_t num_splits, void *workspace,
+                                       size_t workspace_bytes, rswa_decode_graph_t **graph);
+RSWA_API rswa_status_t rswa_decode_graph_launch(const rswa_decode_graph_t *graph, void *stream);
+RSWA_API rswa_status_t rswa_decode_graph_destroy(rswa_decode_graph_t *graph);
 
 /*
  * Synchronise `stream`, read the cache's device error word into *flags

@@ -44,7 +44,8 @@ RSWA_DEVERR_PACK = 16
 EXPORTED = ("rswa_abi_version", "rswa_status_str", "rswa_cache_init", "rswa_append_kv",
             "rswa_decode_workspace_size", "rswa_decode_attn", "rswa_masked_attn",
             "rswa_masked_attn_varlen", "rswa_prefill", "rswa_masked_bwd_workspace_size",
-            "rswa_masked_attn_bwd", "rswa_check_device_error")
+            "rswa_masked_attn_bwd", "rswa_decode_graph_create", "rswa_decode_graph_launch",
+            "rswa_decode_graph_destroy", "rswa_check_device_error")
 
 
 class RswaError(RuntimeError):
@@ -96,6 +97,9 @@ def _lib() -> ctypes.CDLL:
             "rswa_masked_bwd_workspace_size": (SZ, [I32, I32, I32, I32]),
             "rswa_masked_attn_bwd": (I32, [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
                                            I32, F, I32, P, SZ, P]),
+            "rswa_decode_graph_create": (I32, [D, I32, P, P, P, P, F, I32, P, SZ, ctypes.POINTER(P)]),
+            "rswa_decode_graph_launch": (I32, [P, P]),
+            "rswa_decode_graph_destroy": (I32, [P]),
             "rswa_check_device_error": (I32, [D, ctypes.POINTER(I32), P]),
         }
         for name, (res, args) in sig.items():
@@ -221,6 +225,50 @@ def rswa_masked_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, seq_len: int, ref_
                                      int(num_parts), _ptr(workspace), int(workspace_bytes),
                                      _stream(stream))
     return _check(st, "rswa_masked_attn_bwd") if check else st
+
+
+def _ptr_array(items):
+    if items is None:
+        return None
+    arr = (ctypes.c_void_p * len(items))(*[_ptr(t) for t in items])
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+def rswa_decode_graph_create(descs, q, out, k_new=None, v_new=None, scale: float = 0.0,
+                             num_splits: int = 0, workspace=None, workspace_bytes: int | None = None,
+                             check=True):
+    """Returns (status, handle). descs: sequence of CacheDesc, one per layer; q, out,
+    k_new, v_new: sequences of per-layer device tensors (k_new/v_new may be None)."""
+    L = len(descs)
+    arr = (CacheDesc * L)(*descs)
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    keep = []
+    ptrs = []
+    for items in (q, out, k_new, v_new):
+        if items is None:
+            ptrs.append(None)
+        else:
+            p, a = _ptr_array(items)
+            keep.append(a)
+            ptrs.append(p)
+    handle = ctypes.c_void_p(None)
+    st = _lib().rswa_decode_graph_create(arr, L, *ptrs, float(scale), int(num_splits), _ptr(workspace),
+                                         int(workspace_bytes), ctypes.byref(handle))
+    if check:
+        _check(st, "rswa_decode_graph_create")
+    return st, handle.value
+
+
+def rswa_decode_graph_launch(handle, stream=None, check=True) -> int:
+    st = _lib().rswa_decode_graph_launch(handle, _stream(stream))
+    return _check(st, "rswa_decode_graph_launch") if check else st
+
+
+def rswa_decode_graph_destroy(handle, check=True) -> int:
+    st = _lib().rswa_decode_graph_destroy(handle)
+    return _check(st, "rswa_decode_graph_destroy") if check else st
 
 
 def rswa_check_device_error(desc: CacheDesc, stream=None) -> int:

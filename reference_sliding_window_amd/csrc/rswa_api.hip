@@ -416,6 +416,77 @@ rswa_status_t rswa_masked_attn_bwd(const void *q, const void *k, const void *v, 
   return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
 }
 
+struct rswa_decode_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+  int32_t layers;
+};
+
+rswa_status_t rswa_decode_graph_create(const rswa_cache_t *caches, int32_t num_layers,
+                                       const void *const *q, void *const *out,
+                                       const void *const *k_new, const void *const *v_new,
+                                       float scale, int32_t num_splits, void *workspace,
+                                       size_t workspace_bytes, rswa_decode_graph_t **graph) {
+  if (graph == nullptr) return RSWA_ERR_NULL;
+  *graph = nullptr;
+  if (caches == nullptr || q == nullptr || out == nullptr) return RSWA_ERR_NULL;
+  if ((k_new == nullptr) != (v_new == nullptr)) return RSWA_ERR_NULL;
+  if (num_layers < 1) return RSWA_ERR_SHAPE;
+  // Every layer is validated before anything is captured.
+  for (int32_t l = 0; l < num_layers; ++l) {
+    const rswa_cache_t *c = &caches[l];
+    rswa_status_t st = check_cache(c);
+    if (st != RSWA_OK) return st;
+    if (q[l] == nullptr || out[l] == nullptr) return RSWA_ERR_NULL;
+    if (k_new != nullptr && ((k_new[l] == nullptr) != (v_new[l] == nullptr))) return RSWA_ERR_NULL;
+    if (!aligned16(q[l]) || !aligned16(out[l])) return RSWA_ERR_ALIGN;
+    if (k_new != nullptr && k_new[l] != nullptr && (!aligned16(k_new[l]) || !aligned16(v_new[l])))
+      return RSWA_ERR_ALIGN;
+    if (!isfinite(scale) || num_splits < 0) return RSWA_ERR_SHAPE;
+    if (workspace == nullptr || workspace_bytes < rswa_decode_workspace_size(c, num_splits))
+      return RSWA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return RSWA_ERR_ALIGN;
+  }
+  hipStream_t s = nullptr;
+  if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return RSWA_ERR_HIP;
+  if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    (void)hipStreamDestroy(s);
+    return RSWA_ERR_HIP;
+  }
+  rswa_status_t st = RSWA_OK;
+  for (int32_t l = 0; l < num_layers && st == RSWA_OK; ++l)
+    st = rswa_decode_attn(&caches[l], q[l], out[l], k_new != nullptr ? k_new[l] : nullptr,
+                          v_new != nullptr ? v_new[l] : nullptr, scale, num_splits, workspace,
+                          workspace_bytes, s);
+  hipGraph_t g = nullptr;
+  const hipError_t ec = hipStreamEndCapture(s, &g);
+  (void)hipStreamDestroy(s);
+  if (st != RSWA_OK || ec != hipSuccess || g == nullptr) {
+    if (g != nullptr) (void)hipGraphDestroy(g);
+    return st != RSWA_OK ? st : RSWA_ERR_HIP;
+  }
+  hipGraphExec_t exec = nullptr;
+  if (hipGraphInstantiate(&exec, g, nullptr, nullptr, 0) != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return RSWA_ERR_HIP;
+  }
+  *graph = new rswa_decode_graph{g, exec, num_layers};
+  return RSWA_OK;
+}
+
+rswa_status_t rswa_decode_graph_launch(const rswa_decode_graph_t *graph, void *stream) {
+  if (graph == nullptr) return RSWA_ERR_NULL;
+  return hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream)) == hipSuccess ? RSWA_OK
+                                                                                      : RSWA_ERR_HIP;
+}
+
+rswa_status_t rswa_decode_graph_destroy(rswa_decode_graph_t *graph) {
+  if (graph == nullptr) return RSWA_OK;
+  const bool ok = hipGraphExecDestroy(graph->exec) == hipSuccess && hipGraphDestroy(graph->graph) == hipSuccess;
+  delete graph;
+  return ok ? RSWA_OK : RSWA_ERR_HIP;
+}
+
 rswa_status_t rswa_check_device_error(const rswa_cache_t *cache, int32_t *flags, void *stream) {
   if (cache == nullptr || cache->error == nullptr || flags == nullptr) return RSWA_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);

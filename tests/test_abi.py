@@ -176,6 +176,28 @@ def test_prefill_argument_checks():
     assert p(scale=math.inf) == rs.RSWA_ERR_SHAPE
 
 
+def test_decode_graph_argument_checks():
+    """Validation happens before any stream or capture is created."""
+    desc = good_desc()
+    ws = rs.rswa_decode_workspace_size(desc, 0)
+    g = lambda **kw: rs.rswa_decode_graph_create(**{**dict(descs=[desc, desc], q=[A, A], out=[A, A],
+                                                           workspace=A, workspace_bytes=ws), **kw},
+                                                 check=False)[0]
+    assert g(q=[A, None]) == rs.RSWA_ERR_NULL
+    assert g(out=[None, A]) == rs.RSWA_ERR_NULL
+    assert g(k_new=[A, A]) == rs.RSWA_ERR_NULL            # k_new without v_new
+    assert g(k_new=[A, None], v_new=[A, A]) == rs.RSWA_ERR_NULL
+    assert g(q=[A, A + 8]) == rs.RSWA_ERR_ALIGN
+    assert g(descs=[desc, good_desc(head_dim=96)]) == rs.RSWA_ERR_UNSUPPORTED
+    assert g(workspace_bytes=ws - 1) == rs.RSWA_ERR_WORKSPACE
+    assert g(workspace=None, workspace_bytes=0) == rs.RSWA_ERR_WORKSPACE
+    assert g(scale=math.nan) == rs.RSWA_ERR_SHAPE
+    assert g(num_splits=-2) == rs.RSWA_ERR_SHAPE
+    assert g(descs=[], q=[], out=[]) == rs.RSWA_ERR_SHAPE
+    assert rs.rswa_decode_graph_destroy(None) == rs.RSWA_OK
+    assert rs.rswa_decode_graph_launch(None, check=False) == rs.RSWA_ERR_NULL
+
+
 def test_masked_bwd_workspace_size():
     ws = rs.rswa_masked_bwd_workspace_size
     assert ws(-1, 0, 2) == 0
