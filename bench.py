@@ -125,6 +125,122 @@ def cpu_baseline(w, kref, vref, T, budget_s):
                       f"host has {len(os.sched_getaffinity(0))} cores available"}
 
 
+def device_facts(torch):
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "total_memory_GiB": round(p.total_memory / 2 ** 30, 1),
+            "l2_cache_MiB_reported": round(getattr(p, "L2_cache_size", 0) / 2 ** 20, 1)}
+
+
+def probe_read_GBps(torch, rs, stream, nbytes=4 << 30):
+    """Achievable streaming-read rate with the decode kernel's access pattern (buffer > 256 MB MALL)."""
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(1024, dtype=torch.float32, device="cuda")
+    run = lambda i: rs.rswa_probe_stream_read(buf, nbytes, sink, 0, stream=stream)
+    for _ in range(3):
+        run(0)
+    ms = event_time_ms(run, 10, stream) / 10
+    del buf, sink
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def gemm_tflops(torch, stream, m=8192):
+    """A large bf16 GEMM through the vendor library: the measured matrix-core reference."""
+    a = torch.randn((m, m), device="cuda").to(torch.bfloat16)
+    b = torch.randn((m, m), device="cuda").to(torch.bfloat16)
+    c = torch.empty((m, m), device="cuda", dtype=torch.bfloat16)
+    run = lambda i: torch.matmul(a, b, out=c)
+    for _ in range(3):
+        run(0)
+    ms = event_time_ms(run, 10, stream) / 10
+    del a, b, c
+    return 2 * m ** 3 / (ms * 1e-3) / 1e12
+
+
+class _OneRow:
+    """Indexes like the full Q array for one row (the oracle reads only that row)."""
+
+    def __init__(self, row, i, shape):
+        self.row, self.i, self.shape = row, i, shape
+
+    def __getitem__(self, i):
+        assert int(i) == self.i
+        return self.row
+
+
+def cpu_masked_rows(mw, Q, K, V, budget_s):
+    """Time the oracle's packed forward on a few output rows (all heads) and scale to all rows."""
+    import oracle.rswa as orc
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    K64, V64 = wl.to_f64(K, "bf16"), wl.to_f64(V, "bf16")
+    rng = np.random.default_rng(1)
+    rows = rng.integers(mw.ref_len, mw.seq_len, 64)
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        done, t0 = 0, time.perf_counter()
+        while done < len(rows) and time.perf_counter() - t0 < budget_s:
+            i = int(rows[done])
+            orc.masked_attention_rows(_OneRow(wl.to_f64(Q[i], "bf16"), i, Q.shape), K64, V64, [i], mw.ref_len,
+                                      mw.window, mw.scale)
+            done += 1
+        el = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    per_row = el / done
+    return {"seconds_per_output_row_all_heads": per_row,
+            "extrapolated_seconds_for_all_rows": per_row * mw.seq_len, "cores": 1, "kind": "oracle",
+            "sample": f"{done} random output rows x {mw.heads} heads in {el:.1f} s on 1 thread; output rows "
+                      f"see the most keys, so the extrapolation to all {mw.seq_len} rows is an upper bound"}
+
+
+def per_step_curve(torch, rs, w, stream, Tmax):
+    """Per-step duration of the fused decode step over T = 1 .. Tmax for the R-SWA cache and for a
+    full-attention cache (L_m + Tmax slots), each step bracketed by HIP events: the shape of the
+    pages' per-call kernel-duration figure."""
+    B, H, d, L, n = w.batch, w.heads, w.head_dim, w.ref_len, w.window
+    out = torch.empty((B, H, d), dtype=torch.bfloat16, device="cuda")
+    curves = {}
+    for name, window in (("rswa", n), ("full_attention", Tmax)):
+        c = rs.KVCache.allocate([L] * B, H, d, window, dtype=rs.RSWA_BF16)
+        c.k.normal_(0.0, w.sigma_kv)
+        c.v.normal_(0.0, w.sigma_kv)
+        c.step.zero_()
+        ws = c.workspace()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(Tmax)]
+        for c0 in range(0, Tmax, 512):
+            c1 = min(Tmax, c0 + 512)
+            x = torch.randn((3, c1 - c0, B, H, d), device="cuda").to(torch.bfloat16)
+            for t in range(c0, c1):
+                ev[t][0].record(stream)
+                rs.rswa_decode_attn(c.desc, x[0, t - c0], out, x[1, t - c0], x[2, t - c0], 0.0, 0, ws,
+                                    stream=stream)
+                ev[t][1].record(stream)
+            torch.cuda.synchronize()
+            del x
+        ms = np.array([a.elapsed_time(b) for a, b in ev])
+        bins = []
+        for b0 in range(0, Tmax, 256):
+            v = ms[b0:b0 + 256]
+            bins.append({"T": f"{b0 + 1}..{min(Tmax, b0 + 256)}", "median_ms": float(np.median(v)),
+                         "p10_ms": float(np.percentile(v, 10)), "p90_ms": float(np.percentile(v, 90)),
+                         "max_ms": float(v.max())})
+        curves[name] = {"bins": bins, "total_s": float(ms.sum() / 1e3),
+                        "steady_median_ms": float(np.median(ms[n:])),
+                        "tokens_per_s_whole_run": B * Tmax / (ms.sum() / 1e3)}
+        if rs.rswa_check_device_error(c.desc):
+            print("per-step curve reported device errors", file=sys.stderr)
+            sys.exit(1)
+        del c, ws
+    return curves
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +252,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the contrast and masked lines")
     ap.add_argument("--layers", type=int, default=12,
                     help="attention layers in the multi-layer graph line (the pages do not state the count)")
+    ap.add_argument("--curve", action="store_true",
+                    help="also time every fused decode step T = 1..6144, R-SWA and full attention")
     ap.add_argument("--copy-reference", action="store_true",
                     help="first run a plain 1 GiB device copy 3 times (scale reference for HBM counters)")
     args = ap.parse_args()
@@ -205,6 +323,7 @@ def main():
     alg_bytes = sum(decode_bytes(B, H, d, L, n, T) for T in range(W + 1, W + K + 1)) / K
     achieved = alg_bytes / (ms_per_step * 1e-3) / 1e9
     traffic = read_traffic(1)
+    achievable = probe_read_GBps(torch, rs, stream)
     result = {
         "metric": METRIC,
         "value": B / (ms_per_step * 1e-3),
@@ -226,7 +345,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "rswa decode step (split-K attention + split merge), one call",
-                     "algorithmic_bytes_per_launch": alg_bytes},
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "achievable_read_GBps": achievable, "frac_of_achievable": achieved / achievable},
+        "device": device_facts(torch),
     }
     del qs, ks, vs
 
@@ -255,6 +376,40 @@ def main():
             "full_attention_per_T": contrast,
             "rswa_attend_only_ms": ms_r,
             "rswa_fused_step_ms": ms_per_step}
+        # ragged batch: 64 sequences, each with its own pages and decode position, one fused step
+        rw = wl.RAGGED_64
+        rdraw = wl.ragged_lengths(rw)
+        rrefs = [int(x) for x in rdraw.ref_len]
+        rtnow = [int(x) for x in rdraw.t_now]
+        rc = rs.KVCache.allocate(rrefs, rw.heads, rw.head_dim, rw.window, dtype=rs.RSWA_BF16)
+        rc.k.normal_()
+        rc.v.normal_()
+        saved = torch.tensor([t - 1 for t in rtnow], dtype=torch.int32, device="cuda")
+        rq, rk, rv = (torch.randn((rw.batch, rw.heads, rw.head_dim), device="cuda").to(torch.bfloat16)
+                      for _ in range(3))
+        rout = torch.empty_like(rq)
+        rws = rc.workspace()
+
+        def ragged_step(i):
+            rc.step.copy_(saved)   # back to the state before output t_now (idempotent rewrite)
+            rs.rswa_decode_attn(rc.desc, rq, rout, rk, rv, 0.0, 0, rws, stream=stream)
+
+        for _ in range(3):
+            ragged_step(0)
+        ms_rg = event_time_ms(ragged_step, 50, stream) / 50
+        if rs.rswa_check_device_error(rc.desc):
+            print("ragged step reported device errors", file=sys.stderr)
+            sys.exit(1)
+        rbytes = sum(rw.heads * (Lb + min(rw.window, t)) * rw.head_dim * 2 * 2 for Lb, t in zip(rrefs, rtnow)) \
+            + 4 * rw.batch * rw.heads * rw.head_dim * 2
+        result["ragged_64"] = {
+            "workload": rw.name, "batch": rw.batch, "ms_per_step": ms_rg, "tokens_per_s": rw.batch / (ms_rg * 1e-3),
+            "algorithmic_bytes": rbytes, "GBps": rbytes / (ms_rg * 1e-3) / 1e9,
+            "frac_of_peak": rbytes / (ms_rg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "note": "includes a 256-byte step-counter restore before each step"}
+        del rc, rq, rk, rv, rout, rws
+
+        gemm = gemm_tflops(torch, stream)
         # packed 32K masked forward (matrix cores)
         mw = wl.PACKED_32K
         Q, Kp, Vp = wl.packed_qkv(mw)
@@ -271,7 +426,8 @@ def main():
             fl = masked_flops(mw.seq_len, mw.ref_len, mw.window, mw.heads, mw.head_dim,
                               mode == rs.RSWA_PREFIX_FULL)
             masked[name] = {"ms": ms_m, "algorithmic_flop": fl, "TFLOPs": fl / (ms_m * 1e-3) / 1e12,
-                            "frac_of_bf16_peak": fl / (ms_m * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+                            "frac_of_bf16_peak": fl / (ms_m * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                            "frac_of_measured_gemm": fl / (ms_m * 1e-3) / 1e12 / gemm}
         # packed 32K backward (dQ, dK, dV) of the causal-prefix forward
         Gd = to_d(wl.packed_dout(mw))
         lse = torch.empty((mw.heads, mw.seq_len), dtype=torch.float32, device="cuda")
@@ -296,7 +452,10 @@ def main():
             "calls": "lse-producing forward excluded; pre-pass, dQ, dK/dV and reduction kernels included"}
         del Gd, dq, dk, dv, ws_b
         result["masked_32k"] = {"workload": mw.name, "seq_len": mw.seq_len, "ref_len": mw.ref_len,
-                                "window": mw.window, "heads": mw.heads, **masked}
+                                "window": mw.window, "heads": mw.heads,
+                                "measured_bf16_gemm_TFLOPs": gemm, "gemm": "8192^3 bf16 torch.matmul", **masked}
+        if not args.no_cpu_baseline:
+            result["cpu_baseline_masked"] = cpu_masked_rows(mw, Q, Kp, Vp, min(10.0, args.cpu_seconds))
 
         # several documents per 32K pack (samples independent), forward on matrix cores
         cu, refs = wl.varlen_pack_layout(mw.seq_len, mw.base_seed)
@@ -412,6 +571,8 @@ def main():
             "rswa_fused_step_ms": ms_rf, "rswa_fused_tokens_per_s": B / (ms_rf * 1e-3)}
         del r_caches, ws_r, gq, gk, gv, gout
 
+    if args.curve:
+        result["per_step_curve"] = per_step_curve(torch, rs, w, stream, w.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, kref, vref, W + K, args.cpu_seconds)
     result["setup_s"] = setup_s

@@ -309,6 +309,18 @@ RSWA_API rswa_status_t rswa_decode_graph_launch(const rswa_decode_graph_t *graph
 RSWA_API rswa_status_t rswa_decode_graph_destroy(rswa_decode_graph_t *graph);
 
 /*
+ * Measurement helper, not part of the attention path: streams `bytes` (a
+ * multiple of 16) from device buffer `buf` with the decode kernel's access
+ * pattern (16-byte non-temporal loads, 1 KB contiguous per wave instruction),
+ * writing one value per workgroup to `sink` (device float [workgroups], 1024
+ * entries when workgroups = 0, which picks 4 per CU) so that the loads are not
+ * optimised away.
+ * Timing it gives the achievable read rate that bounds rswa_decode_attn.
+ */
+RSWA_API rswa_status_t rswa_probe_stream_read(const void *buf, size_t bytes, float *sink,
+                                     int32_t workgroups, void *stream);
+
+/*
  * Synchronise `stream`, read the cache's device error word into *flags
  * (RSWA_DEVERR_* bits, 0 = none) and clear it. Returns RSWA_ERR_STATE when a
  * bit was set, RSWA_OK otherwise.

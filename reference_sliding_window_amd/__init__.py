@@ -45,7 +45,7 @@ EXPORTED = ("rswa_abi_version", "rswa_status_str", "rswa_cache_init", "rswa_appe
             "rswa_decode_workspace_size", "rswa_decode_attn", "rswa_masked_attn",
             "rswa_masked_attn_varlen", "rswa_prefill", "rswa_masked_bwd_workspace_size",
             "rswa_masked_attn_bwd", "rswa_decode_graph_create", "rswa_decode_graph_launch",
-            "rswa_decode_graph_destroy", "rswa_check_device_error")
+            "rswa_decode_graph_destroy", "rswa_probe_stream_read", "rswa_check_device_error")
 
 
 class RswaError(RuntimeError):
@@ -100,6 +100,7 @@ def _lib() -> ctypes.CDLL:
             "rswa_decode_graph_create": (I32, [D, I32, P, P, P, P, F, I32, P, SZ, ctypes.POINTER(P)]),
             "rswa_decode_graph_launch": (I32, [P, P]),
             "rswa_decode_graph_destroy": (I32, [P]),
+            "rswa_probe_stream_read": (I32, [P, SZ, P, I32, P]),
             "rswa_check_device_error": (I32, [D, ctypes.POINTER(I32), P]),
         }
         for name, (res, args) in sig.items():
@@ -269,6 +270,11 @@ def rswa_decode_graph_launch(handle, stream=None, check=True) -> int:
 def rswa_decode_graph_destroy(handle, check=True) -> int:
     st = _lib().rswa_decode_graph_destroy(handle)
     return _check(st, "rswa_decode_graph_destroy") if check else st
+
+
+def rswa_probe_stream_read(buf, nbytes: int, sink, workgroups: int = 0, stream=None, check=True) -> int:
+    st = _lib().rswa_probe_stream_read(_ptr(buf), int(nbytes), _ptr(sink), int(workgroups), _stream(stream))
+    return _check(st, "rswa_probe_stream_read") if check else st
 
 
 def rswa_check_device_error(desc: CacheDesc, stream=None) -> int:

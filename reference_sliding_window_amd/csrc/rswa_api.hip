@@ -487,6 +487,17 @@ rswa_status_t rswa_decode_graph_destroy(rswa_decode_graph_t *graph) {
   return ok ? RSWA_OK : RSWA_ERR_HIP;
 }
 
+rswa_status_t rswa_probe_stream_read(const void *buf, size_t bytes, float *sink, int32_t workgroups,
+                                     void *stream) {
+  if (buf == nullptr || sink == nullptr) return RSWA_ERR_NULL;
+  if (bytes % 16 != 0 || workgroups < 0) return RSWA_ERR_SHAPE;
+  if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return RSWA_ERR_ALIGN;
+  if (bytes == 0) return RSWA_OK;
+  const hipError_t e = launch_probe_read(buf, bytes, sink, workgroups == 0 ? 1024 : workgroups,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
+}
+
 rswa_status_t rswa_check_device_error(const rswa_cache_t *cache, int32_t *flags, void *stream) {
   if (cache == nullptr || cache->error == nullptr || flags == nullptr) return RSWA_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);

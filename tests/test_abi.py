@@ -198,6 +198,17 @@ def test_decode_graph_argument_checks():
     assert rs.rswa_decode_graph_launch(None, check=False) == rs.RSWA_ERR_NULL
 
 
+def test_probe_argument_checks():
+    pr = lambda **kw: rs.rswa_probe_stream_read(**{**dict(buf=A, nbytes=1 << 20, sink=A + 64), **kw}, check=False)
+    assert pr(buf=None) == rs.RSWA_ERR_NULL
+    assert pr(sink=None) == rs.RSWA_ERR_NULL
+    assert pr(nbytes=1000) == rs.RSWA_ERR_SHAPE
+    assert pr(workgroups=-1) == rs.RSWA_ERR_SHAPE
+    assert pr(buf=A + 8) == rs.RSWA_ERR_ALIGN
+    assert pr(sink=A + 2) == rs.RSWA_ERR_ALIGN
+    assert pr(nbytes=0) == rs.RSWA_OK
+
+
 def test_masked_bwd_workspace_size():
     ws = rs.rswa_masked_bwd_workspace_size
     assert ws(-1, 0, 2) == 0
