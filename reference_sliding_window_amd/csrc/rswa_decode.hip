@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   if (threadIdx.x == 0) p.step[b] = T0 + 1;
 }
 
-// Split-K decode. Grid (splits, H, B), 4 waves. Workgroup (b, h, sp) owns the
+// Split-K decode. Grid (H, B, splits), 4 waves. Workgroup (b, h, sp) owns the
 // key slots [sp*chunk, min(vis, (sp+1)*chunk)) of (b, h), vis = L_m + min(n, T).
 // Its waves take tiles of kRpl*U rows round-robin; lane group g (kLpr lanes)
 // of a wave follows rows g, g + kRpl, ... of each tile with its own online
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   constexpr int kTile = kRpl * U;
   constexpr int kWaves = 4;
 
-  const int b = blockIdx.z, h = blockIdx.y, sp = blockIdx.x;
+  const int b = blockIdx.y, h = blockIdx.x, sp = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane / kLpr, c = lane % kLpr;
   const int64_t bh = (int64_t)b * p.heads + h;
@@ -408,7 +408,10 @@ __global__ void clear_word_kernel(int32_t *w) { *w = 0; }
 template <class E, int D>
 hipError_t launch_decode_t(const DecodeParams &p, hipStream_t s) {
   constexpr int kU = RSWA_DECODE_U;
-  dim3 grid(p.splits, p.heads, p.batch);
+  // Heads fastest: workgroup i lands on XCD i mod 8, so every sequence's chunks
+  // spread over all XCDs whatever the split count (in a ragged batch the later
+  // chunks are often empty; with splits fastest they would pile onto a few XCDs).
+  dim3 grid(p.heads, p.batch, p.splits);
   hipLaunchKernelGGL((decode_split_kernel<E, D, kU>), grid, dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
