@@ -77,12 +77,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
   const bool full_prefix = p.prefix_mode == RSWA_PREFIX_FULL;
   const int nqb = (p.max_seq_len + kBM - 1) / kBM;
   const int G = p.num_seqs * H * nqb;
-  // XCD-aware order: logical work item w -> (sample, head, query block), so that
-  // the query blocks of one (sample, head) share an XCD and its L2.
+  // XCD-aware order: logical work item w -> (head, sample, query block). An XCD
+  // takes a contiguous range of w: the query blocks of one (sample, head) share
+  // its L2, and with heads outermost every XCD gets the same heads of every
+  // sample, so samples of different sizes do not unbalance the XCDs.
   int w = blockIdx.x;
   if ((G & 7) == 0) w = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  const int sample = w / (H * nqb);
-  const int h = (w / nqb) % H;
+  const int h = w / (p.num_seqs * nqb);
+  const int sample = (w / nqb) % p.num_seqs;
   const int q0 = (w % nqb) * kBM;
   // One sample of the pack: rows [row0, row0 + N) with its own reference
   // length; no row sees another sample's keys.
