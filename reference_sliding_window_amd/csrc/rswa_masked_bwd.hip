@@ -12,10 +12,12 @@
 //    block walk; per 32-key tile S^T = K Q^T and dP^T = V dO^T on matrix cores
 //    (K and V row fragments from LDS, Q and dO rows resident), dS^T in
 //    registers, dQ^T += K^T dS^T with K^T from transposing LDS reads;
-//  * bwd_dkdv_kernel: one workgroup per 128 keys x head, 4 waves x 32 keys with
-//    their K and V rows resident; it walks the 32-row query blocks that see any
-//    of its keys: S = Q K^T and dP = dO V^T (Q, dO row fragments from LDS),
-//    dV += P^T dO and dK += dS^T Q with dO and Q from transposing LDS reads.
+//  * bwd_dkdv_kernel: one workgroup per 128 keys x head walking the 32-row
+//    query blocks that see any of its keys; producer waves (K and V rows of 32
+//    keys resident) form S = Q K^T and dP = dO V^T (Q, dO row fragments from
+//    LDS) and P, dS; consumer waves (dK, dV of the same keys resident) take P
+//    and dS through LDS and run dV += P^T dO and dK += dS^T Q with dO and Q
+//    from transposing LDS reads.
 // Q/dO and K/V tiles reach LDS by DMA (global_load_lds_dwordx4), double
 // buffered, into 256-byte rows with swizzled 16-byte chunks (rswa_tile.h).
 #include <hip/hip_runtime.h>
@@ -278,9 +280,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(MaskedBwdParams p) {
 }
 
 // ------------------------------------------------------------- dK/dV kernel
-constexpr int kBK = 128;    // keys per workgroup (4 waves x 32)
+constexpr int kBK = 128;    // keys per workgroup (4 key groups x 32)
 constexpr int kBQ = 32;     // query rows per block
-constexpr int kStages = 4;  // LDS ring of query blocks: one in use, one computed ahead, two in flight
+constexpr int kStages = 5;  // LDS ring of query blocks (see the step comment below)
 
 struct DkdvStage {
   uint16_t q[kBQ * kD];
@@ -288,14 +290,33 @@ struct DkdvStage {
   float ld[2 * kBQ];  // the block's rows: lse in base 2, then D
 };
 
+// P and dS of one query block, already in the layout of the dV/dK products'
+// A operand: per key group, 16-row step and lane, 8 bf16 values (the lane's
+// key against 8 rows of the step).
+struct DkdvXchg {
+  u32x4_t pd[4][2][2][64];  // [key group][16-row step][P, dS][lane]
+};
+
+// s_waitcnt with only lgkmcnt = 0 (this wave's LDS accesses performed).
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
 // Work of one workgroup: 128 keys of one head and a run of query blocks.
 // Key blocks that hold reference-segment keys are seen by every later row; their
 // walk is cut into `parts` runs of equal length whose fp32 partial sums a
 // reduction adds up (parts > 1). Tasks are dealt to the 8 XCDs (block index mod
 // 8) so that each (head, part) lands whole on one XCD, its key blocks walking the
 // same Q/dO rows through one L2; the short output-segment tasks follow.
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
+//
+// Eight waves in two roles, one of each per SIMD: producer wave g (0..3) keeps
+// the K and V rows of key group g resident, forms S and dP of a query block on
+// the matrix cores and turns them into P and dS; consumer wave 4 + g keeps the
+// dK and dV accumulators of the same 32 keys and runs the dV += P^T dO and
+// dK += dS^T Q products of the block before, its A operands passed through LDS
+// lane for lane. Each role fits in half the register file, so the SIMD overlaps
+// one wave's exponentials and LDS reads with the other's products.
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
   __shared__ DkdvStage sm[kStages];
+  __shared__ DkdvXchg xc[2];
   const int N = p.seq_len, H = p.heads, Lm = p.ref_len, n = p.window;
   const bool full_prefix = p.prefix_mode == RSWA_PREFIX_FULL;
   const int S = p.parts, nkb_pre = p.nkb_pre, nkb_win = p.nkb_win;
@@ -322,27 +343,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
   const int kmax = min(N, kw0 + kBK) - 1;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = wave & 3;
   const int hi = lane >> 5, l32 = lane & 31;
   const uint32_t stride = (uint32_t)H * kD;
   const uint16_t *Qg = static_cast<const uint16_t *>(p.q) + (int64_t)h * kD;
-  const uint16_t *Kg = static_cast<const uint16_t *>(p.k) + (int64_t)h * kD;
-  const uint16_t *Vg = static_cast<const uint16_t *>(p.v) + (int64_t)h * kD;
   const uint16_t *Gg = static_cast<const uint16_t *>(p.dout) + (int64_t)h * kD;
-
-  // This lane's key (B operand column / accumulator column of S and dP).
-  const int kj = kw0 + 32 * wave + l32;
-  const bool k_ok = kj < N;
-  bf16x8_t kf[kD / 16], vf[kD / 16];
-  {
-    const int64_t r = (int64_t)(k_ok ? kj : 0) * stride;
-#pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) {
-      const u32x4_t zero = {0, 0, 0, 0};
-      kf[ks] = as_bf16x8(k_ok ? *reinterpret_cast<const u32x4_t *>(Kg + r + ks * 16 + hi * 8) : zero);
-      vf[ks] = as_bf16x8(k_ok ? *reinterpret_cast<const u32x4_t *>(Vg + r + ks * 16 + hi * 8) : zero);
-    }
-  }
-  const bool key_is_prefix = kj < Lm;
 
   // Query blocks whose rows see some key of this workgroup, then this part of them.
   int b_lo, b_hi;
@@ -359,185 +364,261 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
     b_hi = b_lo + (int)((int64_t)len * (part + 1) / S);
     b_lo = s0;
   }
-  const int nblocks = b_hi - b_lo;
-  // Blocks that hide no (query, key) pair: all keys in the reference segment,
-  // all rows output rows, block whole.
-  int clear_lo = nblocks, clear_hi = nblocks;
-  if (kmax < Lm) {
-    clear_lo = min(nblocks, max(0, (Lm + kBQ - 1) / kBQ - b_lo));
-    clear_hi = min(nblocks, max(clear_lo, N / kBQ - b_lo));
+  const int nblocks = max(0, b_hi - b_lo);
+  const float *lse2_h = p.lse2 + (int64_t)h * p.n_pad;
+  const float *d_h = p.d_row + (int64_t)h * p.n_pad;
+
+  // DMA of one 32-row query block: wave w fills rows 4 w .. 4 w + 3 of the Q and
+  // dO tiles (2 instructions) and, with its lanes 8 w .. 8 w + 7, an eighth of
+  // the lse/D strip (1 instruction): 3 per wave and block.
+  auto dma_block = [&](int bi, int stg) __attribute__((always_inline)) {
+    const int qb0 = (b_lo + bi) * kBQ;
+    DkdvStage &st = sm[stg];
+    const int row0 = 4 * wave;
+    const int r = min(qb0 + row0 + (lane >> 4), N - 1);
+    const uint32_t off = __umul24((uint32_t)r, stride);
+    dma_rows(Qg + off, lane, row0, st.q);
+    dma_rows(Gg + off, lane, row0, st.g);
+    if ((lane >> 3) == wave) {
+      const float *src = lane < 32 ? lse2_h + qb0 + lane : d_h + qb0 + (lane - 32);
+      dma4(src, lds_addr(st.ld));  // lane L's dword lands at st.ld[L]
+    }
+  };
+  auto ring = [](int s, int k) __attribute__((always_inline)) { return s + k < kStages ? s + k : s + k - kStages; };
+
+  // Step t (t = 0 .. nblocks, both roles, one barrier each): the producers form
+  // P/dS of block t (its S/dP computed in step t - 1) next to S/dP of block
+  // t + 1; the consumers run the products of block t - 1. Live stages: t - 1,
+  // t (its lse/D strip), t + 1; the other kStages - 3 hold blocks in flight
+  // (DMA of block t + kStages - 2 issued in step t into the stage block t - 2
+  // held, whose last reader finished in step t - 1). Step t's wait: this wave's
+  // part of block t + 1 landed (loads return in order: the three instructions
+  // of each later block may be outstanding); the barrier then makes every
+  // wave's part visible, and P/dS of block t - 1 (written in step t - 1).
+  constexpr int kAhead = kStages - 2;
+  // Waits until at most nb blocks (three instructions each) of this wave's DMA
+  // are outstanding.
+  auto wait_blocks = [](int nb) __attribute__((always_inline)) {
+    static_assert(kAhead <= 5, "vmcnt immediates below");
+    if (nb <= 0)
+      wait_vmcnt<0>();
+    else if (nb == 1)
+      wait_vmcnt<3>();
+    else if (nb == 2)
+      wait_vmcnt<6>();
+    else if (nb == 3)
+      wait_vmcnt<9>();
+    else if (nb == 4)
+      wait_vmcnt<12>();
+    else
+      wait_vmcnt<15>();
+  };
+  auto step_sync = [&](int t, int stg) __attribute__((always_inline)) {
+    wait_blocks(min(kAhead - 2, nblocks - t - 2));
+    wait_lgkmcnt0();
+    block_barrier();
+    if (t + kAhead < nblocks) dma_block(t + kAhead, ring(stg, kAhead));
+  };
+  // Step -1: blocks 0 .. kAhead - 1 requested, wait for block 0.
+  auto first_sync = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j)
+      if (j < nblocks) dma_block(j, j);
+    wait_blocks(min(kAhead - 1, nblocks - 1));
+    block_barrier();
+  };
+
+  if (wave < 4) {
+    // ------------------------------------------------------------ producer
+    const uint16_t *Kg = static_cast<const uint16_t *>(p.k) + (int64_t)h * kD;
+    const uint16_t *Vg = static_cast<const uint16_t *>(p.v) + (int64_t)h * kD;
+    // This lane's key (B operand column / accumulator column of S and dP).
+    const int kj = kw0 + 32 * grp + l32;
+    const bool k_ok = kj < N;
+    bf16x8_t kf[kD / 16], vf[kD / 16];
+    {
+      const int64_t r = (int64_t)(k_ok ? kj : 0) * stride;
+#pragma unroll
+      for (int ks = 0; ks < kD / 16; ++ks) {
+        const u32x4_t zero = {0, 0, 0, 0};
+        kf[ks] = as_bf16x8(k_ok ? *reinterpret_cast<const u32x4_t *>(Kg + r + ks * 16 + hi * 8) : zero);
+        vf[ks] = as_bf16x8(k_ok ? *reinterpret_cast<const u32x4_t *>(Vg + r + ks * 16 + hi * 8) : zero);
+      }
+    }
+    // Blocks that hide no (query, key) pair: all keys in the reference segment,
+    // all rows output rows, block whole.
+    int clear_lo = nblocks, clear_hi = nblocks;
+    if (kmax < Lm) {
+      clear_lo = min(nblocks, max(0, (Lm + kBQ - 1) / kBQ - b_lo));
+      clear_hi = min(nblocks, max(clear_lo, N / kBQ - b_lo));
+    }
+    // Rows the lane's key is visible to form one interval [v_lo, v_hi): the whole
+    // sequence tail from the key (reference-segment key), plus every row below
+    // L_m with the full-prefix mode, or the n rows from the key (output key).
+    const bool key_is_prefix = kj < Lm;
+    int v_lo = kj, v_hi = key_is_prefix ? N : min(N, kj + n);
+    if (key_is_prefix && full_prefix) v_lo = 0;
+    if (!k_ok) v_hi = v_lo;
+    const uint32_t v_span = (uint32_t)(v_hi - v_lo);
+    uint32_t roff[kD / 16];
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) roff[ks] = row_frag_off(l32, hi, ks);
+    const float c = p.scale_log2;
+
+    // S = Q K^T and dP = dO V^T of the block in stage stg: element r is query
+    // qb0 + 8 (r/4) + 4 hi + r%4 of that block, key kj.
+    auto sdp = [&](int stg, f32x16_t &s, f32x16_t &dp) __attribute__((always_inline)) {
+      const char *qb = reinterpret_cast<const char *>(sm[stg].q);
+      const char *gb = reinterpret_cast<const char *>(sm[stg].g);
+#pragma unroll
+      for (int ks = 0; ks < kD / 16; ++ks) {
+        const bf16x8_t qa = as_bf16x8(*reinterpret_cast<const u32x4_t *>(qb + roff[ks]));
+        const bf16x8_t ga = as_bf16x8(*reinterpret_cast<const u32x4_t *>(gb + roff[ks]));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], ks == 0 ? f32x16_t{} : s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], ks == 0 ? f32x16_t{} : dp, 0, 0, 0);
+      }
+    };
+
+    // Producer step t: P and dS of block t (stage stg) from S/dP computed the
+    // step before, two elements per k-step of block t + 1's S/dP products (about
+    // the two products' time), order fixed by hand (sched_barrier).
+    auto produce = [&](int t, int stg, f32x16_t &s_cur, f32x16_t &dp_cur, f32x16_t &s_nxt, f32x16_t &dp_nxt)
+        __attribute__((always_inline)) {
+      step_sync(t, stg);
+      const int qb0 = (b_lo + t) * kBQ;
+      const DkdvStage &st = sm[stg];
+      float xs[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xs[r] = s_cur[r];
+      if (t < clear_lo || t >= clear_hi) {
+        const uint32_t tt = (uint32_t)(qb0 + 4 * hi - v_lo);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          xs[r] = tt + (uint32_t)(8 * (r >> 2) + (r & 3)) < v_span ? xs[r] : kNegInf;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // lse/D of this block's rows 8 g + 4 hi .. + 3 (broadcast reads).
+      f32x4_t l4[4], d4[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        l4[g] = *reinterpret_cast<const f32x4_t *>(&st.ld[8 * g + 4 * hi]);
+        d4[g] = *reinterpret_cast<const f32x4_t *>(&st.ld[kBQ + 8 * g + 4 * hi]);
+      }
+      // S/dP of block t + 1 (a stale stage after the last block; result unused).
+      const int nstg = ring(stg, 1);
+      const char *qn = reinterpret_cast<const char *>(sm[nstg].q);
+      const char *gn = reinterpret_cast<const char *>(sm[nstg].g);
+      bf16x8_t qa[kD / 16], ga[kD / 16];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        qa[ks] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(qn + roff[ks]));
+        ga[ks] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(gn + roff[ks]));
+      }
+      uint32_t pw[8], dw[8];
+#pragma unroll
+      for (int ks = 0; ks < kD / 16; ++ks) {
+        if (ks + 2 < kD / 16) {
+          qa[ks + 2] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(qn + roff[ks + 2]));
+          ga[ks + 2] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(gn + roff[ks + 2]));
+        }
+        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], ks == 0 ? f32x16_t{} : s_nxt, 0, 0, 0);
+        dp_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[ks], vf[ks], ks == 0 ? f32x16_t{} : dp_nxt, 0, 0, 0);
+        // elements 2 ks, 2 ks + 1: rows 8 (ks/2) + 4 hi + 2 (ks%2) + {0, 1}
+        const int g = ks >> 1, e = 2 * (ks & 1);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(xs[2 * ks], c, -l4[g][e]));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(xs[2 * ks + 1], c, -l4[g][e + 1]));
+        pw[ks] = pack_bf16(p0, p1);
+        dw[ks] = pack_bf16(p0 * (dp_cur[2 * ks] - d4[g][e]), p1 * (dp_cur[2 * ks + 1] - d4[g][e + 1]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // Step st2 of the consumer's products uses elements 8 st2 .. 8 st2 + 7.
+      DkdvXchg &xo = xc[t & 1];
+#pragma unroll
+      for (int st2 = 0; st2 < 2; ++st2) {
+        xo.pd[grp][st2][0][lane] = u32x4_t{pw[4 * st2], pw[4 * st2 + 1], pw[4 * st2 + 2], pw[4 * st2 + 3]};
+        xo.pd[grp][st2][1][lane] = u32x4_t{dw[4 * st2], dw[4 * st2 + 1], dw[4 * st2 + 2], dw[4 * st2 + 3]};
+      }
+    };
+
+    if (nblocks == 0) return;
+    f32x16_t sa = {}, dpa = {}, sb = {}, dpb = {};
+    first_sync();
+    sdp(0, sa, dpa);
+    int t = 0, stg = 0;
+    for (; t + 1 < nblocks; t += 2) {
+      produce(t, stg, sa, dpa, sb, dpb);
+      stg = ring(stg, 1);
+      produce(t + 1, stg, sb, dpb, sa, dpa);
+      stg = ring(stg, 1);
+    }
+    if (t < nblocks) {
+      produce(t, stg, sa, dpa, sb, dpb);
+      stg = ring(stg, 1);
+    }
+    step_sync(nblocks, stg);  // hands P/dS of the last block to the consumers
+    return;
   }
 
+  // -------------------------------------------------------------- consumer
   f32x16_t dk[kD / 32], dv[kD / 32];
 #pragma unroll
   for (int j = 0; j < kD / 32; ++j) {
     dk[j] = f32x16_t{};
     dv[j] = f32x16_t{};
   }
-  uint32_t roff[kD / 16], toff[kD / 32][2];
-#pragma unroll
-  for (int ks = 0; ks < kD / 16; ++ks) roff[ks] = row_frag_off(l32, hi, ks);
+  uint32_t toff[kD / 32][2];
 #pragma unroll
   for (int db = 0; db < kD / 32; ++db) {
     toff[db][0] = tr_off(lane, db, 0);
     toff[db][1] = tr_off(lane, db, 1);
   }
-  const float c = p.scale_log2;
-  const float *lse2_h = p.lse2 + (int64_t)h * p.n_pad;
-  const float *d_h = p.d_row + (int64_t)h * p.n_pad;
-
-  // DMA of one 32-row query block: wave w fills rows 8 w .. 8 w + 7 of the Q and
-  // dO tiles (4 instructions) and, with its lanes 16 w .. 16 w + 15, a quarter
-  // of the lse/D strip (1 instruction): 5 per wave and block.
-  auto dma_block = [&](int qb0, DkdvStage &st) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int row0 = 8 * wave + 4 * j;
-      const int r = min(qb0 + row0 + (lane >> 4), N - 1);
-      const uint32_t off = __umul24((uint32_t)r, stride);
-      dma_rows(Qg + off, lane, row0, st.q);
-      dma_rows(Gg + off, lane, row0, st.g);
-    }
-    if ((lane >> 4) == wave) {
-      const float *src = lane < 32 ? lse2_h + qb0 + lane : d_h + qb0 + (lane - 32);
-      dma4(src, lds_addr(st.ld));  // lane L's dword lands at st.ld[L]
-    }
-  };
-
-  // S = Q K^T and dP = dO V^T of the block in stage stg: element r is query
-  // qb0 + 8 (r/4) + 4 hi + r%4 of that block, key kj.
-  auto sdp = [&](int stg, f32x16_t &s, f32x16_t &dp) __attribute__((always_inline)) {
+  // dV += P^T dO and dK += dS^T Q of the block in stage stg over two 16-row
+  // steps (st2 = j / 4, d block db = j % 4); the transposing reads run two
+  // products ahead (order fixed by hand with sched_barrier).
+  auto consume = [&](int stg, const DkdvXchg &xi) __attribute__((always_inline)) {
     const char *qb = reinterpret_cast<const char *>(sm[stg].q);
     const char *gb = reinterpret_cast<const char *>(sm[stg].g);
+    bf16x8_t pa[2], da[2], tg[8], tq[8];
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) {
-      const bf16x8_t qa = as_bf16x8(*reinterpret_cast<const u32x4_t *>(qb + roff[ks]));
-      const bf16x8_t ga = as_bf16x8(*reinterpret_cast<const u32x4_t *>(gb + roff[ks]));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], ks == 0 ? f32x16_t{} : s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], ks == 0 ? f32x16_t{} : dp, 0, 0, 0);
+    for (int st2 = 0; st2 < 2; ++st2) {
+      pa[st2] = as_bf16x8(xi.pd[grp][st2][0][lane]);
+      da[st2] = as_bf16x8(xi.pd[grp][st2][1][lane]);
     }
-  };
-
-  // Rows each lane's key is visible to form one interval [v_lo, v_hi): the whole
-  // sequence tail from the key (reference-segment key), plus every row below
-  // L_m with the full-prefix mode, or the n rows from the key (output key).
-  int v_lo = kj, v_hi = key_is_prefix ? N : min(N, kj + n);
-  if (key_is_prefix && full_prefix) v_lo = 0;
-  if (!k_ok) v_hi = v_lo;
-  const uint32_t v_span = (uint32_t)(v_hi - v_lo);
-
-  // One pipeline step for block bi (in stage bi & 3), whose S and dP were
-  // computed the step before: wait for block bi + 1, start the DMA of block
-  // bi + 3, then S/dP of block bi + 1 on the matrix cores interleaved with this
-  // block's P and dS (two elements per k-step, about the two products' time),
-  // then dV += P^T dO and dK += dS^T Q. The order is fixed by hand
-  // (sched_barrier): the compiler's own schedule serialises the two units.
-  auto step = [&](int bi, f32x16_t &s_cur, f32x16_t &dp_cur, f32x16_t &s_nxt, f32x16_t &dp_nxt)
-      __attribute__((always_inline)) {
-    const int qb0 = (b_lo + bi) * kBQ;
-    const DkdvStage &st = sm[bi & 3];
-    // Loads return in order: with only block bi + 2's five outstanding, this
-    // wave's part of block bi + 1 has landed.
-    if (bi + 2 < nblocks)
-      wait_vmcnt<5>();
-    else
-      wait_vmcnt<0>();
-    block_barrier();  // every wave's part landed; stage (bi + 3) & 3 is no longer read
-    if (bi + 3 < nblocks) dma_block(qb0 + 3 * kBQ, sm[(bi + 3) & 3]);
-    float xs[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) xs[r] = s_cur[r];
-    if (bi < clear_lo || bi >= clear_hi) {
-      const uint32_t t = (uint32_t)(qb0 + 4 * hi - v_lo);
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        xs[r] = t + (uint32_t)(8 * (r >> 2) + (r & 3)) < v_span ? xs[r] : kNegInf;
+    for (int j = 0; j < 2; ++j) {
+      tg[j] = tr_operand(gb, toff[j][0], toff[j][1], 0);
+      tq[j] = tr_operand(qb, toff[j][0], toff[j][1], 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // lse/D of this block's rows 8 g + 4 hi .. + 3 (broadcast reads).
-    f32x4_t l4[4], d4[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      l4[g] = *reinterpret_cast<const f32x4_t *>(&st.ld[8 * g + 4 * hi]);
-      d4[g] = *reinterpret_cast<const f32x4_t *>(&st.ld[kBQ + 8 * g + 4 * hi]);
-    }
-    // S/dP of block bi + 1 (a stale stage after the last block; result unused).
-    const char *qn = reinterpret_cast<const char *>(sm[(bi + 1) & 3].q);
-    const char *gn = reinterpret_cast<const char *>(sm[(bi + 1) & 3].g);
-    bf16x8_t qa[kD / 16], ga[kD / 16];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      qa[ks] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(qn + roff[ks]));
-      ga[ks] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(gn + roff[ks]));
-    }
-    uint32_t pw[8], dw[8];
-#pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) {
-      if (ks + 2 < kD / 16) {
-        qa[ks + 2] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(qn + roff[ks + 2]));
-        ga[ks + 2] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(gn + roff[ks + 2]));
-      }
-      s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], ks == 0 ? f32x16_t{} : s_nxt, 0, 0, 0);
-      dp_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[ks], vf[ks], ks == 0 ? f32x16_t{} : dp_nxt, 0, 0, 0);
-      // elements 2 ks, 2 ks + 1: rows 8 (ks/2) + 4 hi + 2 (ks%2) + {0, 1}
-      const int g = ks >> 1, e = 2 * (ks & 1);
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(xs[2 * ks], c, -l4[g][e]));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(xs[2 * ks + 1], c, -l4[g][e + 1]));
-      pw[ks] = pack_bf16(p0, p1);
-      dw[ks] = pack_bf16(p0 * (dp_cur[2 * ks] - d4[g][e]), p1 * (dp_cur[2 * ks + 1] - d4[g][e + 1]));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // dV += P^T dO and dK += dS^T Q over two 16-query steps; step st2 uses
-    // elements 8 st2 .. 8 st2 + 7 (queries 16 st2 + {4 hi.., 8 + 4 hi..}).
-    // Transposing reads run one (st2, db) pair ahead of their products.
-    const char *qb = reinterpret_cast<const char *>(st.q);
-    const char *gb = reinterpret_cast<const char *>(st.g);
-    bf16x8_t tg[2], tq[2];
-    tg[0] = tr_operand(gb, toff[0][0], toff[0][1], 0);
-    tq[0] = tr_operand(qb, toff[0][0], toff[0][1], 0);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int st2 = j >> 2, db = j & 3;
-      if (j + 1 < 8) {
-        const int st2n = (j + 1) >> 2, dbn = (j + 1) & 3;
-        tg[(j + 1) & 1] = tr_operand(gb, toff[dbn][0], toff[dbn][1], st2n);
-        tq[(j + 1) & 1] = tr_operand(qb, toff[dbn][0], toff[dbn][1], st2n);
+      if (j + 2 < 8) {
+        const int jn = j + 2;
+        tg[jn] = tr_operand(gb, toff[jn & 3][0], toff[jn & 3][1], jn >> 2);
+        tq[jn] = tr_operand(qb, toff[jn & 3][0], toff[jn & 3][1], jn >> 2);
       }
-      const bf16x8_t pa = as_bf16x8(u32x4_t{pw[4 * st2], pw[4 * st2 + 1], pw[4 * st2 + 2], pw[4 * st2 + 3]});
-      const bf16x8_t da = as_bf16x8(u32x4_t{dw[4 * st2], dw[4 * st2 + 1], dw[4 * st2 + 2], dw[4 * st2 + 3]});
-      dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, tg[j & 1], dv[db], 0, 0, 0);
-      dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, tq[j & 1], dk[db], 0, 0, 0);
+      dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[st2], tg[j], dv[db], 0, 0, 0);
+      dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[st2], tq[j], dk[db], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-
-  wait_vmcnt<0>();  // resident K/V rows landed (the compiler does not count the DMA)
-#pragma unroll
-  for (int j = 0; j < 3; ++j)
-    if (j < nblocks) dma_block((b_lo + j) * kBQ, sm[j]);
-  f32x16_t sa = {}, dpa = {}, sb = {}, dpb = {};
   if (nblocks > 0) {
-    // block 0 landed: blocks 1 and 2 (five instructions each) may be outstanding
-    if (nblocks > 2)
-      wait_vmcnt<10>();
-    else if (nblocks > 1)
-      wait_vmcnt<5>();
-    else
-      wait_vmcnt<0>();
-    block_barrier();
-    sdp(0, sa, dpa);
+    first_sync();
+    int stg = 0;
+    step_sync(0, stg);
+    for (int t = 1; t <= nblocks; ++t) {
+      const int prev = stg;
+      stg = ring(stg, 1);
+      step_sync(t, stg);
+      consume(prev, xc[(t - 1) & 1]);
+    }
   }
-  int bi = 0;
-  for (; bi + 1 < nblocks; bi += 2) {
-    step(bi, sa, dpa, sb, dpb);
-    step(bi + 1, sb, dpb, sa, dpa);
-  }
-  if (bi < nblocks) step(bi, sa, dpa, sb, dpb);
 
-  // Accumulator element r of dk[db] is key kw0 + 32 wave + 8 (r/4) + 4 hi + r%4
+  // Accumulator element r of dk[db] is key kw0 + 32 grp + 8 (r/4) + 4 hi + r%4
   // and d = 32 db + l32: every lane stores, whatever its own score column.
   if (part >= 0 && S > 1) {
-    const int64_t base = (((int64_t)part * H + h) * p.kpre + kw0 + 32 * wave) * kD;
+    const int64_t base = (((int64_t)part * H + h) * p.kpre + kw0 + 32 * grp) * kD;
     float *pk = p.part_dk + base;
     float *pv = p.part_dv + base;
 #pragma unroll
@@ -556,7 +637,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
   uint16_t *dvg = static_cast<uint16_t *>(p.dv) + (int64_t)h * kD;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int key = kw0 + 32 * wave + 8 * (r >> 2) + 4 * hi + (r & 3);
+    const int key = kw0 + 32 * grp + 8 * (r >> 2) + 4 * hi + (r & 3);
     if (key >= N) continue;
 #pragma unroll
     for (int db = 0; db < kD / 32; ++db) {
@@ -612,7 +693,7 @@ hipError_t launch_masked_bwd(const MaskedBwdParams &p, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t gk = masked_bwd_dkdv_grid(p.heads, p.parts, p.nkb_pre, p.nkb_win);
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)gk), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)gk), dim3(512), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess || p.parts == 1 || p.nkb_pre == 0) return e;
   const int64_t kval = p.seq_len < p.kpre ? p.seq_len : p.kpre;
