@@ -450,7 +450,7 @@ def main():
                                "dQ); the kernels execute seven (S and dP are formed in both the dQ and "
                                "the dK/dV pass)",
             "calls": "lse-producing forward excluded; pre-pass, dQ, dK/dV and reduction kernels included"}
-        del Gd, dq, dk, dv, ws_b
+        del ws_b
         result["masked_32k"] = {"workload": mw.name, "seq_len": mw.seq_len, "ref_len": mw.ref_len,
                                 "window": mw.window, "heads": mw.heads,
                                 "measured_bf16_gemm_TFLOPs": gemm, "gemm": "8192^3 bf16 torch.matmul", **masked}
@@ -470,13 +470,31 @@ def main():
         ms_v = event_time_ms(run_v, 20, stream) / 20
         fl_v = sum(masked_flops(int(N_s), int(L_s), mw.window, mw.heads, mw.head_dim, False)
                    for N_s, L_s in zip(lens, refs))
+        # backward of the same pack (dO as for the single-sequence backward)
+        rs.rswa_masked_attn_varlen(Qd, Kd, Vd, Od, cu_d, refs_d, len(refs), mw.seq_len, int(lens.max()),
+                                   mw.window, mw.heads, mw.head_dim, rs.RSWA_BF16, rs.RSWA_PREFIX_CAUSAL, 0.0,
+                                   stream=stream, lse=lse)
+        ws_v = torch.empty(rs.rswa_masked_bwd_varlen_workspace_size(mw.seq_len, mw.heads), dtype=torch.uint8,
+                           device="cuda")
+        run_vb = lambda i: rs.rswa_masked_attn_bwd_varlen(Qd, Kd, Vd, Od, Gd, lse, dq, dk, dv, cu_d, refs_d,
+                                                          len(refs), mw.seq_len, int(lens.max()), mw.window,
+                                                          mw.heads, mw.head_dim, rs.RSWA_BF16,
+                                                          rs.RSWA_PREFIX_CAUSAL, 0.0, ws_v, stream=stream)
+        for _ in range(3):
+            run_vb(0)
+        ms_vb = event_time_ms(run_vb, 10, stream) / 10
         result["varlen_32k"] = {
             "workload": "packed-32k-varlen-bf16", "samples": len(refs),
             "sample_rows": [int(x) for x in lens], "ref_lens": [int(x) for x in refs],
             "layout": "pages ~ U{2..16} (L = 256 pages + 32), outputs ~ U{256..2048}, filled front to back",
             "ms": ms_v, "algorithmic_flop": fl_v, "TFLOPs": fl_v / (ms_v * 1e-3) / 1e12,
-            "frac_of_bf16_peak": fl_v / (ms_v * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
-        del Qd, Kd, Vd, Od, cu_d, refs_d
+            "frac_of_bf16_peak": fl_v / (ms_v * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "backward": {"ms": ms_vb, "algorithmic_flop": 2.5 * fl_v,
+                         "TFLOPs": 2.5 * fl_v / (ms_vb * 1e-3) / 1e12,
+                         "frac_of_bf16_peak": 2.5 * fl_v / (ms_vb * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                         "calls": "rswa_masked_attn_bwd_varlen (pre-pass, dQ, dK/dV); flop convention as "
+                                  "for the single-sequence backward"}}
+        del Qd, Kd, Vd, Od, cu_d, refs_d, Gd, dq, dk, dv, lse, ws_v
 
         # prefill -> decode hand-off at the 40-page decode shape: B sequences of L_m reference
         # rows plus T0 = n outputs (the window full at hand-off), one call for the whole batch

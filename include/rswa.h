@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RSWA_ABI_VERSION 4
+#define RSWA_ABI_VERSION 5
 
 #if defined(__GNUC__)
 #define RSWA_API __attribute__((visibility("default")))
@@ -274,6 +274,43 @@ RSWA_API rswa_status_t rswa_masked_attn_bwd(const void *q, const void *k, const 
                                    int32_t head_dim, int32_t dtype, int32_t prefix_mode,
                                    float scale, int32_t num_parts, void *workspace,
                                    size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of device workspace rswa_masked_attn_bwd_varlen needs for a pack of
+ * total_tokens rows. 0 for invalid sizes.
+ */
+RSWA_API size_t rswa_masked_bwd_varlen_workspace_size(int32_t total_tokens, int32_t num_heads);
+
+/*
+ * rswa_masked_attn_bwd over a pack of independent samples: the backward of
+ * rswa_masked_attn_varlen for the loss sum(dout * out). Training runs on
+ * samples of 1 to 50 pages up to a 32K-token length (WeThinkIn page, section
+ * 实验与证据, 训练设置); a pack lets one call take a batch of them unpadded.
+ * Each sample gets exactly the single-sequence gradients of its own rows.
+ *  q, k, v, out, dout  device [total_tokens][num_heads][head_dim] bf16; out
+ *               and lse come from rswa_masked_attn_varlen with the same
+ *               cu_seqlens, ref_lens, sizes, window, mode and scale.
+ *  lse          device float [num_heads][total_tokens] from that call.
+ *  cu_seqlens, ref_lens, num_seqs, total_tokens, max_seq_len
+ *               as for rswa_masked_attn_varlen (device int32 arrays).
+ *  dq, dk, dv   device [total_tokens][num_heads][head_dim] bf16. Every row of
+ *               every valid sample is written (keys no row sees get zero);
+ *               rows outside every sample, and the rows of a sample whose
+ *               metadata are invalid, are left as they were. Must not alias
+ *               the inputs.
+ *  workspace    device, 16-byte aligned, >= rswa_masked_bwd_varlen_workspace_size
+ *               bytes; its contents on entry do not matter.
+ * Same restrictions as rswa_masked_attn_bwd; no atomics, repeated calls give
+ * identical bits, and a pack of one sample gives the bits of
+ * rswa_masked_attn_bwd whenever that call runs in one part (seq_len up to
+ * 8192 rows with num_parts 0).
+ */
+RSWA_API rswa_status_t rswa_masked_attn_bwd_varlen(
+    const void *q, const void *k, const void *v, const void *out, const void *dout,
+    const float *lse, void *dq, void *dk, void *dv, const int32_t *cu_seqlens,
+    const int32_t *ref_lens, int32_t num_seqs, int32_t total_tokens, int32_t max_seq_len,
+    int32_t window, int32_t num_heads, int32_t head_dim, int32_t dtype, int32_t prefix_mode,
+    float scale, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * A decode step through several attention layers as one HIP graph. A decoder

@@ -44,7 +44,8 @@ RSWA_DEVERR_PACK = 16
 EXPORTED = ("rswa_abi_version", "rswa_status_str", "rswa_cache_init", "rswa_append_kv",
             "rswa_decode_workspace_size", "rswa_decode_attn", "rswa_masked_attn",
             "rswa_masked_attn_varlen", "rswa_prefill", "rswa_masked_bwd_workspace_size",
-            "rswa_masked_attn_bwd", "rswa_decode_graph_create", "rswa_decode_graph_launch",
+            "rswa_masked_attn_bwd", "rswa_masked_bwd_varlen_workspace_size",
+            "rswa_masked_attn_bwd_varlen", "rswa_decode_graph_create", "rswa_decode_graph_launch",
             "rswa_decode_graph_destroy", "rswa_probe_stream_read", "rswa_check_device_error")
 
 
@@ -97,6 +98,9 @@ def _lib() -> ctypes.CDLL:
             "rswa_masked_bwd_workspace_size": (SZ, [I32, I32, I32, I32]),
             "rswa_masked_attn_bwd": (I32, [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
                                            I32, F, I32, P, SZ, P]),
+            "rswa_masked_bwd_varlen_workspace_size": (SZ, [I32, I32]),
+            "rswa_masked_attn_bwd_varlen": (I32, [P, P, P, P, P, P, P, P, P, P, P, I32, I32, I32, I32,
+                                                  I32, I32, I32, I32, F, P, SZ, P]),
             "rswa_decode_graph_create": (I32, [D, I32, P, P, P, P, F, I32, P, SZ, ctypes.POINTER(P)]),
             "rswa_decode_graph_launch": (I32, [P, P]),
             "rswa_decode_graph_destroy": (I32, [P]),
@@ -226,6 +230,28 @@ def rswa_masked_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, seq_len: int, ref_
                                      int(num_parts), _ptr(workspace), int(workspace_bytes),
                                      _stream(stream))
     return _check(st, "rswa_masked_attn_bwd") if check else st
+
+
+def rswa_masked_bwd_varlen_workspace_size(total_tokens: int, num_heads: int) -> int:
+    return _lib().rswa_masked_bwd_varlen_workspace_size(total_tokens, num_heads)
+
+
+def rswa_masked_attn_bwd_varlen(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens, ref_lens,
+                                num_seqs: int, total_tokens: int, max_seq_len: int, window: int,
+                                num_heads: int, head_dim: int, dtype: int = RSWA_BF16,
+                                prefix_mode: int = RSWA_PREFIX_CAUSAL, scale: float = 0.0,
+                                workspace=None, workspace_bytes: int | None = None, stream=None,
+                                check=True) -> int:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    st = _lib().rswa_masked_attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens),
+                                            _ptr(ref_lens), num_seqs, total_tokens, max_seq_len,
+                                            window, num_heads, head_dim, dtype, prefix_mode,
+                                            float(scale), _ptr(workspace), int(workspace_bytes),
+                                            _stream(stream))
+    return _check(st, "rswa_masked_attn_bwd_varlen") if check else st
 
 
 def _ptr_array(items):

@@ -424,6 +424,73 @@ rswa_status_t rswa_masked_attn_bwd(const void *q, const void *k, const void *v, 
   return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
 }
 
+size_t rswa_masked_bwd_varlen_workspace_size(int32_t total_tokens, int32_t num_heads) {
+  if (total_tokens < 0 || num_heads < 1) return 0;
+  const size_t n_pad = ((size_t)total_tokens + 31) / 32 * 32;
+  return 2 * (size_t)num_heads * n_pad * sizeof(float);
+}
+
+rswa_status_t rswa_masked_attn_bwd_varlen(const void *q, const void *k, const void *v,
+                                          const void *out, const void *dout, const float *lse,
+                                          void *dq, void *dk, void *dv,
+                                          const int32_t *cu_seqlens, const int32_t *ref_lens,
+                                          int32_t num_seqs, int32_t total_tokens,
+                                          int32_t max_seq_len, int32_t window, int32_t num_heads,
+                                          int32_t head_dim, int32_t dtype, int32_t prefix_mode,
+                                          float scale, void *workspace, size_t workspace_bytes,
+                                          void *stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr ||
+      lse == nullptr || dq == nullptr || dk == nullptr || dv == nullptr || cu_seqlens == nullptr ||
+      ref_lens == nullptr)
+    return RSWA_ERR_NULL;
+  if (num_seqs < 0 || total_tokens < 0 || max_seq_len < 0 || window < 1 || num_heads < 1)
+    return RSWA_ERR_SHAPE;
+  if (dtype != RSWA_BF16 || head_dim != 128) return RSWA_ERR_UNSUPPORTED;
+  if (prefix_mode != RSWA_PREFIX_CAUSAL && prefix_mode != RSWA_PREFIX_FULL)
+    return RSWA_ERR_UNSUPPORTED;
+  if ((int64_t)total_tokens * num_heads * head_dim >= ((int64_t)1 << 31)) return RSWA_ERR_CAPACITY;
+  if ((int64_t)num_seqs * num_heads * ((max_seq_len + 127) / 128) >= ((int64_t)1 << 31))
+    return RSWA_ERR_CAPACITY;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return RSWA_ERR_ALIGN;
+  if (((reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(cu_seqlens) |
+        reinterpret_cast<uintptr_t>(ref_lens)) & 3u) != 0)
+    return RSWA_ERR_ALIGN;
+  if (!isfinite(scale)) return RSWA_ERR_SHAPE;
+  if (num_seqs == 0 || total_tokens == 0 || max_seq_len == 0) return RSWA_OK;
+  const size_t need = rswa_masked_bwd_varlen_workspace_size(total_tokens, num_heads);
+  if (workspace == nullptr) return RSWA_ERR_NULL;
+  if (!aligned16(workspace)) return RSWA_ERR_ALIGN;
+  if (workspace_bytes < need) return RSWA_ERR_WORKSPACE;
+  MaskedBwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.seq_len = total_tokens;
+  p.n_pad = (int32_t)(need / (2 * (size_t)num_heads * sizeof(float)));
+  p.d_row = static_cast<float *>(workspace);
+  p.lse2 = p.d_row + (size_t)num_heads * p.n_pad;
+  p.parts = 1;
+  p.cu_seqlens = cu_seqlens;
+  p.ref_lens = ref_lens;
+  p.num_seqs = num_seqs;
+  p.max_seq_len = max_seq_len;
+  p.window = window;
+  p.heads = num_heads;
+  p.prefix_mode = prefix_mode;
+  p.scale = scale == 0.f ? 1.f / sqrtf((float)head_dim) : scale;
+  p.scale_log2 = p.scale * kLog2e;
+  const hipError_t e = launch_masked_bwd(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
+}
+
 struct rswa_decode_graph {
   hipGraph_t graph;
   hipGraphExec_t exec;

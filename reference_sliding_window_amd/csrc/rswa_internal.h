@@ -126,6 +126,14 @@ struct MaskedBwdParams {
   int32_t kpre;     // 128 * nkb_pre
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
+  // Pack of independent samples (nullptr: one sequence of seq_len rows).
+  // Sample s is rows [cu_seqlens[s], cu_seqlens[s + 1]) with reference length
+  // ref_lens[s] (device arrays); seq_len is then the pack's total rows and
+  // parts is 1.
+  const int32_t *cu_seqlens;
+  const int32_t *ref_lens;
+  int32_t num_seqs;
+  int32_t max_seq_len;
 };
 
 // Launchers (enqueue only; return the launch's hipError_t).

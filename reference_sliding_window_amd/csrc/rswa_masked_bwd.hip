@@ -79,23 +79,38 @@ struct DqStage {
 
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(MaskedBwdParams p) {
   __shared__ DqStage sm[kStagesQ];
-  const int N = p.seq_len, H = p.heads, Lm = p.ref_len, n = p.window;
+  const int H = p.heads, n = p.window;
   const bool full_prefix = p.prefix_mode == RSWA_PREFIX_FULL;
-  const int nqb = (N + kBMq - 1) / kBMq;
-  const int G = nqb * H;
+  const int samples = p.cu_seqlens != nullptr ? p.num_seqs : 1;
+  const int nqb = ((p.cu_seqlens != nullptr ? p.max_seq_len : p.seq_len) + kBMq - 1) / kBMq;
+  const int G = samples * H * nqb;
+  // Work item w -> (head, sample, query block); an XCD takes a contiguous range of w.
   int w = blockIdx.x;
   if ((G & 7) == 0) w = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  const int h = w / nqb;
+  const int h = w / (samples * nqb);
+  const int sample = (w / nqb) % samples;
   const int q0 = (w % nqb) * kBMq;
+  // One sample of a pack: rows [row0, row0 + N) with its own reference length.
+  int row0 = 0, N = p.seq_len, Lm = p.ref_len;
+  if (p.cu_seqlens != nullptr) {
+    row0 = p.cu_seqlens[sample];
+    const int row1 = p.cu_seqlens[sample + 1];
+    Lm = p.ref_lens[sample];
+    N = row1 - row0;
+    // device-side metadata: a malformed sample is skipped
+    if (row0 < 0 || row1 < row0 || row1 > p.seq_len || N > p.max_seq_len || Lm < 0 || Lm > N) return;
+  }
+  if (q0 >= N) return;
   const int q_end = min(N, q0 + kBMq);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi = lane >> 5, l32 = lane & 31;
   const uint32_t stride = (uint32_t)H * kD;
-  const uint16_t *Qg = static_cast<const uint16_t *>(p.q) + (int64_t)h * kD;
-  const uint16_t *Kg = static_cast<const uint16_t *>(p.k) + (int64_t)h * kD;
-  const uint16_t *Vg = static_cast<const uint16_t *>(p.v) + (int64_t)h * kD;
-  const uint16_t *Gg = static_cast<const uint16_t *>(p.dout) + (int64_t)h * kD;
+  const int64_t base = (int64_t)row0 * stride + (int64_t)h * kD;
+  const uint16_t *Qg = static_cast<const uint16_t *>(p.q) + base;
+  const uint16_t *Kg = static_cast<const uint16_t *>(p.k) + base;
+  const uint16_t *Vg = static_cast<const uint16_t *>(p.v) + base;
+  const uint16_t *Gg = static_cast<const uint16_t *>(p.dout) + base;
 
   // Key blocks: the reference segment [0, pre_hi), then the output keys
   // [win_lo, win_hi) some row of this workgroup sees.
@@ -122,7 +137,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(MaskedBwdParams p) {
       gf[ks] = as_bf16x8(q_ok ? *reinterpret_cast<const u32x4_t *>(Gg + r + ks * 16 + hi * 8) : zero);
     }
   }
-  const int64_t rq = (int64_t)h * p.n_pad + (q_ok ? qi : 0);
+  const int64_t rq = (int64_t)h * p.n_pad + row0 + (q_ok ? qi : 0);
   const float lse2 = p.lse2[rq];
   const float Dq = p.d_row[rq];
   const float c = p.scale_log2;
@@ -265,7 +280,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(MaskedBwdParams p) {
 
   if (!q_ok) return;
   // dQ^T accumulator element r of dq[db] is d = 32 db + 8 (r/4) + 4 hi + r%4.
-  uint16_t *orow = static_cast<uint16_t *>(p.dq) + (int64_t)qi * stride + (int64_t)h * kD;
+  uint16_t *orow = static_cast<uint16_t *>(p.dq) + base + (int64_t)qi * stride;
   const float sc = p.scale;
 #pragma unroll
   for (int db = 0; db < kD / 32; ++db) {
@@ -317,27 +332,49 @@ __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
   __shared__ DkdvStage sm[kStages];
   __shared__ DkdvXchg xc[2];
-  const int N = p.seq_len, H = p.heads, Lm = p.ref_len, n = p.window;
+  const int H = p.heads, n = p.window;
   const bool full_prefix = p.prefix_mode == RSWA_PREFIX_FULL;
-  const int S = p.parts, nkb_pre = p.nkb_pre, nkb_win = p.nkb_win;
-  const int x = blockIdx.x & 7, kx = blockIdx.x >> 3;
-  const int pairs = H * S;
-  const int pre_x = (pairs > x ? (pairs - 1 - x) / 8 + 1 : 0) * nkb_pre;
-  const int U = H * nkb_win;
-  const int win_x = U > x ? (U - 1 - x) / 8 + 1 : 0;
+  const int S = p.parts;
+  int N = p.seq_len, Lm = p.ref_len, row0 = 0;
   int h, kb, part;
-  if (kx < pre_x) {
-    const int pr = x + 8 * (kx / nkb_pre);
-    kb = kx % nkb_pre;
-    h = pr / S;
-    part = pr % S;
-  } else {
-    const int k2 = kx - pre_x;
-    if (k2 >= win_x) return;  // padding of this XCD's task list
-    const int u = x + 8 * k2;
-    h = u / nkb_win;
-    kb = nkb_pre + u % nkb_win;
+  if (p.cu_seqlens != nullptr) {
+    // Pack of samples: work item w -> (head, sample, 128-key block), an XCD
+    // taking a contiguous range of w; walks are short, so never split.
+    const int nkb = (p.max_seq_len + kBK - 1) / kBK;
+    const int G = p.num_seqs * H * nkb;
+    int w = blockIdx.x;
+    if ((G & 7) == 0) w = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    h = w / (p.num_seqs * nkb);
+    const int sample = (w / nkb) % p.num_seqs;
+    kb = w % nkb;
     part = -1;
+    row0 = p.cu_seqlens[sample];
+    const int row1 = p.cu_seqlens[sample + 1];
+    Lm = p.ref_lens[sample];
+    N = row1 - row0;
+    // device-side metadata: a malformed sample is skipped
+    if (row0 < 0 || row1 < row0 || row1 > p.seq_len || N > p.max_seq_len || Lm < 0 || Lm > N) return;
+    if (kb * kBK >= N) return;
+  } else {
+    const int nkb_pre = p.nkb_pre, nkb_win = p.nkb_win;
+    const int x = blockIdx.x & 7, kx = blockIdx.x >> 3;
+    const int pairs = H * S;
+    const int pre_x = (pairs > x ? (pairs - 1 - x) / 8 + 1 : 0) * nkb_pre;
+    const int U = H * nkb_win;
+    const int win_x = U > x ? (U - 1 - x) / 8 + 1 : 0;
+    if (kx < pre_x) {
+      const int pr = x + 8 * (kx / nkb_pre);
+      kb = kx % nkb_pre;
+      h = pr / S;
+      part = pr % S;
+    } else {
+      const int k2 = kx - pre_x;
+      if (k2 >= win_x) return;  // padding of this XCD's task list
+      const int u = x + 8 * k2;
+      h = u / nkb_win;
+      kb = nkb_pre + u % nkb_win;
+      part = -1;
+    }
   }
   const int kw0 = kb * kBK;
   const int kmax = min(N, kw0 + kBK) - 1;
@@ -346,8 +383,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
   const int grp = wave & 3;
   const int hi = lane >> 5, l32 = lane & 31;
   const uint32_t stride = (uint32_t)H * kD;
-  const uint16_t *Qg = static_cast<const uint16_t *>(p.q) + (int64_t)h * kD;
-  const uint16_t *Gg = static_cast<const uint16_t *>(p.dout) + (int64_t)h * kD;
+  const int64_t base = (int64_t)row0 * stride + (int64_t)h * kD;
+  const uint16_t *Qg = static_cast<const uint16_t *>(p.q) + base;
+  const uint16_t *Gg = static_cast<const uint16_t *>(p.dout) + base;
 
   // Query blocks whose rows see some key of this workgroup, then this part of them.
   int b_lo, b_hi;
@@ -365,8 +403,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
     b_lo = s0;
   }
   const int nblocks = max(0, b_hi - b_lo);
-  const float *lse2_h = p.lse2 + (int64_t)h * p.n_pad;
-  const float *d_h = p.d_row + (int64_t)h * p.n_pad;
+  const float *lse2_h = p.lse2 + (int64_t)h * p.n_pad + row0;
+  const float *d_h = p.d_row + (int64_t)h * p.n_pad + row0;
 
   // DMA of one 32-row query block: wave w fills rows 4 w .. 4 w + 3 of the Q and
   // dO tiles (2 instructions) and, with its lanes 8 w .. 8 w + 7, an eighth of
@@ -380,7 +418,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
     dma_rows(Qg + off, lane, row0, st.q);
     dma_rows(Gg + off, lane, row0, st.g);
     if ((lane >> 3) == wave) {
-      const float *src = lane < 32 ? lse2_h + qb0 + lane : d_h + qb0 + (lane - 32);
+      // rows past the sequence's end repeat its last row, as the tile rows do
+      // (their scores are masked, so P = dS = 0 whatever finite values sit here)
+      const int rr = min(qb0 + (lane & 31), N - 1);
+      const float *src = lane < 32 ? lse2_h + rr : d_h + rr;
       dma4(src, lds_addr(st.ld));  // lane L's dword lands at st.ld[L]
     }
   };
@@ -430,8 +471,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
 
   if (wave < 4) {
     // ------------------------------------------------------------ producer
-    const uint16_t *Kg = static_cast<const uint16_t *>(p.k) + (int64_t)h * kD;
-    const uint16_t *Vg = static_cast<const uint16_t *>(p.v) + (int64_t)h * kD;
+    const uint16_t *Kg = static_cast<const uint16_t *>(p.k) + base;
+    const uint16_t *Vg = static_cast<const uint16_t *>(p.v) + base;
     // This lane's key (B operand column / accumulator column of S and dP).
     const int kj = kw0 + 32 * grp + l32;
     const bool k_ok = kj < N;
@@ -618,9 +659,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
   // Accumulator element r of dk[db] is key kw0 + 32 grp + 8 (r/4) + 4 hi + r%4
   // and d = 32 db + l32: every lane stores, whatever its own score column.
   if (part >= 0 && S > 1) {
-    const int64_t base = (((int64_t)part * H + h) * p.kpre + kw0 + 32 * grp) * kD;
-    float *pk = p.part_dk + base;
-    float *pv = p.part_dv + base;
+    const int64_t pbase = (((int64_t)part * H + h) * p.kpre + kw0 + 32 * grp) * kD;
+    float *pk = p.part_dk + pbase;
+    float *pv = p.part_dv + pbase;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kl = 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -633,8 +674,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
     return;
   }
   const float sc = p.scale;
-  uint16_t *dkg = static_cast<uint16_t *>(p.dk) + (int64_t)h * kD;
-  uint16_t *dvg = static_cast<uint16_t *>(p.dv) + (int64_t)h * kD;
+  uint16_t *dkg = static_cast<uint16_t *>(p.dk) + base;
+  uint16_t *dvg = static_cast<uint16_t *>(p.dv) + base;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int key = kw0 + 32 * grp + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -688,11 +729,15 @@ hipError_t launch_masked_bwd(const MaskedBwdParams &p, hipStream_t s) {
   hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t gq = (int64_t)((p.seq_len + kBMq - 1) / kBMq) * p.heads;
+  const bool pack = p.cu_seqlens != nullptr;
+  const int64_t rows_max = pack ? p.max_seq_len : p.seq_len;
+  const int64_t samples = pack ? p.num_seqs : 1;
+  const int64_t gq = samples * ((rows_max + kBMq - 1) / kBMq) * p.heads;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)gq), dim3(256), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t gk = masked_bwd_dkdv_grid(p.heads, p.parts, p.nkb_pre, p.nkb_win);
+  const int64_t gk = pack ? samples * p.heads * ((rows_max + kBK - 1) / kBK)
+                          : masked_bwd_dkdv_grid(p.heads, p.parts, p.nkb_pre, p.nkb_win);
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)gk), dim3(512), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess || p.parts == 1 || p.nkb_pre == 0) return e;

@@ -255,6 +255,45 @@ def test_masked_bwd_argument_checks():
     assert b(seq_len=0, ref_len=0, workspace=None, workspace_bytes=0) == rs.RSWA_OK
 
 
+def test_masked_bwd_varlen_workspace_size():
+    # two float rows per head and row of the pack, rows padded to 32
+    assert rs.rswa_masked_bwd_varlen_workspace_size(300, 2) == 2 * 2 * 320 * 4
+    assert rs.rswa_masked_bwd_varlen_workspace_size(0, 3) == 0
+    assert rs.rswa_masked_bwd_varlen_workspace_size(-1, 2) == 0
+    assert rs.rswa_masked_bwd_varlen_workspace_size(64, 0) == 0
+
+
+def test_varlen_bwd_argument_checks():
+    ws = rs.rswa_masked_bwd_varlen_workspace_size(300, 2)
+    base = dict(q=A, k=A, v=A, out=A, dout=A, lse=A, dq=A, dk=A, dv=A, cu_seqlens=A, ref_lens=A,
+                num_seqs=2, total_tokens=300, max_seq_len=200, window=8, num_heads=2, head_dim=128,
+                workspace=A, workspace_bytes=ws)
+    b = lambda **kw: rs.rswa_masked_attn_bwd_varlen(**{**base, **kw}, check=False)
+    for name in ("q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv", "cu_seqlens", "ref_lens"):
+        assert b(**{name: None}) == rs.RSWA_ERR_NULL, name
+    for name in ("q", "k", "v", "out", "dout", "dq", "dk", "dv"):
+        assert b(**{name: A + 8}) == rs.RSWA_ERR_ALIGN, name
+    for name in ("lse", "cu_seqlens", "ref_lens"):
+        assert b(**{name: A + 2}) == rs.RSWA_ERR_ALIGN, name
+    assert b(num_seqs=-1) == rs.RSWA_ERR_SHAPE
+    assert b(total_tokens=-1) == rs.RSWA_ERR_SHAPE
+    assert b(max_seq_len=-1) == rs.RSWA_ERR_SHAPE
+    assert b(window=0) == rs.RSWA_ERR_SHAPE
+    assert b(num_heads=0) == rs.RSWA_ERR_SHAPE
+    assert b(head_dim=64) == rs.RSWA_ERR_UNSUPPORTED
+    assert b(dtype=rs.RSWA_FP32) == rs.RSWA_ERR_UNSUPPORTED
+    assert b(prefix_mode=2) == rs.RSWA_ERR_UNSUPPORTED
+    assert b(scale=math.nan) == rs.RSWA_ERR_SHAPE
+    assert b(total_tokens=2 ** 20, num_heads=16) == rs.RSWA_ERR_CAPACITY
+    assert b(num_seqs=2 ** 20, max_seq_len=2 ** 20, num_heads=16, total_tokens=1) == rs.RSWA_ERR_CAPACITY
+    assert b(workspace=None, workspace_bytes=0) == rs.RSWA_ERR_NULL
+    assert b(workspace_bytes=ws - 1) == rs.RSWA_ERR_WORKSPACE
+    assert b(workspace=A + 4) == rs.RSWA_ERR_ALIGN
+    # nothing to do: no sample, no row or no row per sample
+    for kw in (dict(num_seqs=0), dict(total_tokens=0), dict(max_seq_len=0)):
+        assert b(workspace=None, workspace_bytes=0, **kw) == rs.RSWA_OK, kw
+
+
 def test_check_device_error_null_arguments():
     lib = rs.library()
     flags = ctypes.c_int32(0)
