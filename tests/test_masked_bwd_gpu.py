@@ -197,15 +197,16 @@ def test_backward_medium_every_row_and_key():
 
 
 @pytest.mark.slow
-def test_backward_32k_sampled_and_column_sums():
+@pytest.mark.parametrize("mode", [CAUSAL, FULL])
+def test_backward_32k_sampled_and_column_sums(mode):
     """Full packed 32K size: dQ on sampled rows and dK/dV on sampled output-segment
     keys exactly (the rows that see such a key are the n rows from it on), and for
     every key the column sums the softmax fixes: sum_j dV_j = sum_i dO_i (each
     row's weights sum to one) and sum_j dK_j = 0 (each row's dS sums to zero)."""
     mw = wl.PACKED_32K
     N, L_m, n, H = mw.seq_len, mw.ref_len, mw.window, mw.heads
-    banner(f"packed 32K bwd N={N} L_m={L_m} n={n} H={H}")
-    r = PackedRun(N, L_m, n, H, CAUSAL, seed=mw.base_seed, sigma=mw.sigma)
+    banner(f"packed 32K bwd N={N} L_m={L_m} n={n} H={H} mode={mode}")
+    r = PackedRun(N, L_m, n, H, mode, seed=mw.base_seed, sigma=mw.sigma)
     r.forward()
     r.backward()
     torch.cuda.synchronize()
@@ -217,7 +218,7 @@ def test_backward_32k_sampled_and_column_sums():
     rows = sorted(set([0, 1, L_m - 1, L_m, L_m + 1, L_m + n - 1, L_m + n, 4095, 4096, N - 1] +
                       rng.integers(0, N, 24).tolist()))
     Qr, Gr = _RowView(f(r.Q[rows]), rows), _RowView(f(r.G[rows]), rows)
-    dQ, _, _ = orc.masked_attention_backward(Qr, K, V, Gr, L_m, n, mw.scale, CAUSAL, rows=rows)
+    dQ, _, _ = orc.masked_attention_backward(Qr, K, V, Gr, L_m, n, mw.scale, mode, rows=rows)
     ma, rel = check_grad(dq[rows], dQ, "dQ 32K sampled rows")
     print(f"dQ rows: max|d|={ma:.3e} rel={rel:.3e}")
     # output-segment keys in three runs of 8 (near L_m, mid-sequence, the tail);
@@ -229,7 +230,7 @@ def test_backward_32k_sampled_and_column_sums():
         see = list(range(a, min(N, a + 8 + n - 1)))
         Qs = _RowView(f(r.Q[see])[:, hs], see)
         Gs = _RowView(f(r.G[see])[:, hs], see)
-        _, dK, dV = orc.masked_attention_backward(Qs, Kh, Vh, Gs, L_m, n, mw.scale, CAUSAL, rows=see)
+        _, dK, dV = orc.masked_attention_backward(Qs, Kh, Vh, Gs, L_m, n, mw.scale, mode, rows=see)
         check_grad(dk[a:a + 8][:, hs], dK[a:a + 8], f"dK keys {a}..{a + 7}")
         check_grad(dv[a:a + 8][:, hs], dV[a:a + 8], f"dV keys {a}..{a + 7}")
     # column sums over every key, per head and dimension (fp64 sums of the bf16 results)
