@@ -589,6 +589,74 @@ def main():
             "rswa_fused_step_ms": ms_rf, "rswa_fused_tokens_per_s": B / (ms_rf * 1e-3)}
         del r_caches, ws_r, gq, gk, gv, gout
 
+        # one-page decode (B = 1): 3.4 MB per step, a working set the caches hold, so the step is
+        # bound by launch and kernel latency; fused append + attend steps eagerly and replayed as a
+        # one-layer HIP graph, past the window fill (T > n)
+        ow = wl.ONE_PAGE
+        oc = rs.KVCache.allocate([ow.ref_len], ow.heads, ow.head_dim, ow.window, dtype=rs.RSWA_BF16)
+        oc.k.normal_()
+        oc.v.normal_()
+        oq, ok_, ov = (torch.randn((1, ow.heads, ow.head_dim), device="cuda").to(torch.bfloat16)
+                       for _ in range(3))
+        oout = torch.empty_like(oq)
+        ows = oc.workspace()
+        o_step = lambda i: rs.rswa_decode_attn(oc.desc, oq, oout, ok_, ov, 0.0, 0, ows, stream=stream)
+        for _ in range(2 * ow.window):
+            o_step(0)
+        o_steps = 1024
+        ms_oe = event_time_ms(o_step, o_steps, stream) / o_steps
+        _, g_o = rs.rswa_decode_graph_create([oc.desc], [oq], [oout], [ok_], [ov], workspace=ows)
+        try:
+            for _ in range(16):
+                rs.rswa_decode_graph_launch(g_o, stream=stream)
+            ms_og = event_time_ms(lambda i: rs.rswa_decode_graph_launch(g_o, stream=stream), o_steps,
+                                  stream) / o_steps
+        finally:
+            rs.rswa_decode_graph_destroy(g_o)
+        # the same step through `layers` layers (own cache each): eager calls against one graph launch
+        lcs = [rs.KVCache.allocate([ow.ref_len], ow.heads, ow.head_dim, ow.window, dtype=rs.RSWA_BF16)
+               for _ in range(layers)]
+        for c in lcs:
+            c.k.normal_()
+            c.v.normal_()
+        lq = [torch.randn_like(oq) for _ in range(layers)]
+        lk = [torch.randn_like(oq) for _ in range(layers)]
+        lv = [torch.randn_like(oq) for _ in range(layers)]
+        lo = [torch.empty_like(oq) for _ in range(layers)]
+
+        def l_step(i):
+            for li in range(layers):
+                rs.rswa_decode_attn(lcs[li].desc, lq[li], lo[li], lk[li], lv[li], 0.0, 0, ows, stream=stream)
+
+        for _ in range(2 * ow.window):
+            l_step(0)
+        l_steps = 256
+        ms_le = event_time_ms(l_step, l_steps, stream) / l_steps
+        _, g_l = rs.rswa_decode_graph_create([c.desc for c in lcs], lq, lo, lk, lv, workspace=ows)
+        try:
+            for _ in range(16):
+                rs.rswa_decode_graph_launch(g_l, stream=stream)
+            ms_lg = event_time_ms(lambda i: rs.rswa_decode_graph_launch(g_l, stream=stream), l_steps,
+                                  stream) / l_steps
+        finally:
+            rs.rswa_decode_graph_destroy(g_l)
+        for c in [oc] + lcs:
+            if rs.rswa_check_device_error(c.desc):
+                print("one-page decode reported device errors", file=sys.stderr)
+                sys.exit(1)
+        o_bytes = ow.heads * (ow.ref_len + ow.window) * ow.head_dim * 2 * 2 + 4 * ow.heads * ow.head_dim * 2
+        result["one_page"] = {
+            "workload": ow.name, "batch": 1, "heads": ow.heads, "ref_len": ow.ref_len, "window": ow.window,
+            "bound": "latency (working set far below the 4 MB L2 per XCD and the MALL)",
+            "eager_us_per_step": ms_oe * 1e3, "graph_us_per_step": ms_og * 1e3,
+            "eager_tokens_per_s": 1 / (ms_oe * 1e-3), "graph_tokens_per_s": 1 / (ms_og * 1e-3),
+            "algorithmic_bytes_per_step": o_bytes, "steps_timed": o_steps,
+            "layers": layers, "layers_eager_us_per_step": ms_le * 1e3, "layers_graph_us_per_step": ms_lg * 1e3,
+            "note": f"fused append + attend, split + merge kernels; eager steps T = {2 * ow.window + 1}.."
+                    f"{2 * ow.window + o_steps}, graph steps T = {2 * ow.window + o_steps + 17}.."
+                    f"{2 * ow.window + 2 * o_steps + 16}"}
+        del oc, oq, ok_, ov, oout, ows, lcs, lq, lk, lv, lo
+
     if args.curve:
         result["per_step_curve"] = per_step_curve(torch, rs, w, stream, w.steps)
     if not args.no_cpu_baseline:
