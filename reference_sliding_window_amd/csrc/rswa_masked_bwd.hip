@@ -18,8 +18,11 @@
 //    LDS) and P, dS; consumer waves (dK, dV of the same keys resident) take P
 //    and dS through LDS and run dV += P^T dO and dK += dS^T Q with dO and Q
 //    from transposing LDS reads.
-// Q/dO and K/V tiles reach LDS by DMA (global_load_lds_dwordx4), double
-// buffered, into 256-byte rows with swizzled 16-byte chunks (rswa_tile.h).
+// Q/dO and K/V tiles reach LDS by DMA (global_load_lds_dwordx4) through rings
+// of four (dQ) and five (dK/dV) stages, into 256-byte rows with swizzled
+// 16-byte chunks (rswa_tile.h). The same kernels serve one sequence or a pack
+// of independent samples (device row offsets and reference lengths per
+// sample; a row never sees another sample's keys).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
