@@ -573,14 +573,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
         const float p1 = __builtin_amdgcn_exp2f(fmaf(xs[2 * ks + 1], c, -l4[g][e + 1]));
         pw[ks] = pack_bf16(p0, p1);
         dw[ks] = pack_bf16(p0 * (dp_cur[2 * ks] - d4[g][e]), p1 * (dp_cur[2 * ks + 1] - d4[g][e + 1]));
+        // Step st2 of the consumer's products uses elements 8 st2 .. 8 st2 + 7;
+        // storing each half as soon as it exists keeps the arithmetic between
+        // the products.
+        if ((ks & 3) == 3) {
+          const int st2 = ks >> 2;
+          DkdvXchg &xo = xc[t & 1];
+          xo.pd[grp][st2][0][lane] = u32x4_t{pw[4 * st2], pw[4 * st2 + 1], pw[4 * st2 + 2], pw[4 * st2 + 3]};
+          xo.pd[grp][st2][1][lane] = u32x4_t{dw[4 * st2], dw[4 * st2 + 1], dw[4 * st2 + 2], dw[4 * st2 + 3]};
+        }
         __builtin_amdgcn_sched_barrier(0);
-      }
-      // Step st2 of the consumer's products uses elements 8 st2 .. 8 st2 + 7.
-      DkdvXchg &xo = xc[t & 1];
-#pragma unroll
-      for (int st2 = 0; st2 < 2; ++st2) {
-        xo.pd[grp][st2][0][lane] = u32x4_t{pw[4 * st2], pw[4 * st2 + 1], pw[4 * st2 + 2], pw[4 * st2 + 3]};
-        xo.pd[grp][st2][1][lane] = u32x4_t{dw[4 * st2], dw[4 * st2 + 1], dw[4 * st2 + 2], dw[4 * st2 + 3]};
       }
     };
 
