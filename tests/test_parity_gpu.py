@@ -395,14 +395,15 @@ def test_masked_rows_agree_with_decode_kernel():
 
 
 @pytest.mark.slow
-def test_packed_32k_sampled_rows():
+@pytest.mark.parametrize("mode", [rs.RSWA_PREFIX_CAUSAL, rs.RSWA_PREFIX_FULL])
+def test_packed_32k_sampled_rows(mode):
     mw = wl.PACKED_32K
     N, L_m, n, H = mw.seq_len, mw.ref_len, mw.window, mw.heads
-    banner(f"packed 32K masked forward, N={N} L_m={L_m} n={n} H={H}")
+    banner(f"packed 32K masked forward, N={N} L_m={L_m} n={n} H={H} mode={mode}")
     Q, K, V = wl.packed_qkv(mw)
     out = torch.empty((N, H, 128), dtype=torch.bfloat16, device="cuda")
     Qd, Kd, Vd = (to_dev(x, "bf16") for x in (Q, K, V))
-    rs.rswa_masked_attn(Qd, Kd, Vd, out, N, L_m, n, H, 128, rs.RSWA_BF16, rs.RSWA_PREFIX_CAUSAL, 0.0)
+    rs.rswa_masked_attn(Qd, Kd, Vd, out, N, L_m, n, H, 128, rs.RSWA_BF16, mode, 0.0)
     torch.cuda.synchronize()
     got = to_f64(out)
     rng = np.random.default_rng(11)
@@ -413,8 +414,8 @@ def test_packed_32k_sampled_rows():
     K64 = wl.to_f64(K, "bf16")
     V64 = wl.to_f64(V, "bf16")
     Q64 = wl.to_f64(Q[rows], "bf16")
-    ref = orc.masked_attention_rows(_RowView(Q64, rows), K64, V64, rows, L_m, n, mw.scale)
-    ma, rel = check_close(got[rows], ref, "bf16", "packed 32K sampled rows")
+    ref = orc.masked_attention_rows(_RowView(Q64, rows), K64, V64, rows, L_m, n, mw.scale, mode)
+    ma, rel = check_close(got[rows], ref, "bf16", f"packed 32K sampled rows, mode {mode}")
     print(f"packed 32K: {len(rows)} rows x {H} heads max|d|={ma:.3e} rel={rel:.3e}")
 
 
