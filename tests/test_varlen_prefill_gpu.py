@@ -236,3 +236,62 @@ def test_prefill_flags_bad_sequences_and_keeps_the_rest():
     assert torch.isnan(out[:20].float()).all()
     ref, _ = sample_oracle(Q, K, V, 20, 80, 50, n, CAUSAL)
     check_close(to_f64(out)[20:80], ref, "bf16", "good sequence of a pack with a bad one")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("t0", [128, 200])
+def test_prefill_40page_full_size(t0):
+    """The hand-off at the 40-page decode shape (32 sequences of L_m = 10272 reference rows plus
+    T0 outputs, one call): every sequence's K/V block equals the oracle's ring image built from
+    the packed rows, bit for bit; every step counter is T0; the output equals the plain packed
+    forward of the same pack bit for bit and matches the oracle on sampled rows of two sequences.
+    T0 = n is the configuration the benchmark times; T0 = 200 has wrapped the ring."""
+    w = wl.FORTY_PAGE
+    B, H, L, n = w.batch, w.heads, w.ref_len, w.window
+    rows_b = L + t0
+    total = B * rows_b
+    banner(f"40-page prefill B={B} L_m={L} n={n} T0={t0} rows={total}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.base_seed + t0)
+    q, k, v = (torch.randn((total, H, D), device="cuda", generator=gen).to(torch.bfloat16) for _ in range(3))
+    cu = torch.arange(0, total + 1, rows_b, dtype=torch.int32, device="cuda")
+    cache = rs.KVCache.allocate([L] * B, H, D, n, dtype=rs.RSWA_BF16)
+    cache.k.fill_(float("nan"))
+    cache.v.fill_(float("nan"))
+    cache.step.fill_(-5)
+    out = torch.full_like(q, float("nan"))
+    rs.rswa_prefill(cache.desc, q, k, v, out, cu, total, rows_b, CAUSAL, 0.0)
+    torch.cuda.synchronize()
+    assert rs.rswa_check_device_error(cache.desc) == 0
+    assert cache.step.cpu().tolist() == [t0] * B
+
+    # cache images, compared on the device: slot s of sequence b holds packed row b*rows_b + pos - 1
+    img = orc.ring_image(L, n, t0)
+    assert (img > 0).all()  # T0 >= n: every slot written
+    src = torch.as_tensor(img - 1, dtype=torch.int64, device="cuda")
+    kb, vb = k.view(torch.int16), v.view(torch.int16)
+    ck, cv = cache.k.view(torch.int16), cache.v.view(torch.int16)
+    for b in range(B):
+        rows = src + b * rows_b
+        assert torch.equal(cache.block(ck, b), kb[rows].permute(1, 0, 2)), f"sequence {b} K block"
+        assert torch.equal(cache.block(cv, b), vb[rows].permute(1, 0, 2)), f"sequence {b} V block"
+
+    # the output is the packed forward's: same bits as the forward call alone
+    fwd = torch.full_like(q, float("nan"))
+    refs = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    rs.rswa_masked_attn_varlen(q, k, v, fwd, cu, refs, B, total, rows_b, n, H, D, rs.RSWA_BF16, CAUSAL, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), fwd.view(torch.int16))
+    del fwd
+
+    rng = np.random.default_rng(t0)
+    special = [0, 1, L - 1, L, L + 1, L + n - 2, L + n - 1, rows_b - 1]
+    local = sorted(set(special + rng.integers(0, rows_b, 8).tolist()))
+    for b in (0, B - 1):
+        r0 = b * rows_b
+        f = lambda a: a[r0:r0 + rows_b].float().cpu().numpy().astype(np.float64)
+        Qs, Ks, Vs = f(q), f(k), f(v)
+        ref = orc.masked_attention_rows(Qs, Ks, Vs, local, L, n, SCALE, CAUSAL)
+        got = to_f64(out[r0:r0 + rows_b])[local]
+        ma, rel = check_close(got, ref, "bf16", f"40-page prefill sequence {b} sampled rows")
+        print(f"sequence {b}: {len(local)} rows x {H} heads max|d|={ma:.3e} rel={rel:.3e}", flush=True)
