@@ -224,9 +224,13 @@ RSWA_API rswa_status_t rswa_masked_attn_varlen(const void *q, const void *k, con
  * ref_len[b] + ((t-1) mod window), step[b] = T0_b (yhxrc and 夜雨聆风 pages;
  * WeThinkIn page, Eq. (6)). Decode then continues with output T0_b + 1.
  *  q, k, v, out  device [total_tokens][num_heads][head_dim], cache dtype; only
- *                RSWA_BF16 with head_dim 128 (the packed kernel's case).
- * A sequence whose metadata are invalid gets RSWA_DEVERR_PACK (or the cache's
- * usual bits) in the error word and is left untouched; the forward skips it.
+ *                RSWA_BF16 with head_dim 128 (the packed kernel's case). k and v
+ *                must not overlap the cache pools.
+ * One kernel launch: each forward workgroup also copies the cache-kept rows of
+ * its own query block into the cache. A sequence whose sample does not fit
+ * (RSWA_DEVERR_PACK) or whose cache metadata are invalid (RSWA_DEVERR_REF_LEN,
+ * RSWA_DEVERR_ALIGN) is flagged in the error word and its cache block and step
+ * are left untouched; the rows of every well-formed sample are still computed.
  */
 RSWA_API rswa_status_t rswa_prefill(const rswa_cache_t *cache, const void *q, const void *k,
                            const void *v, void *out, float *lse, const int32_t *cu_seqlens,

@@ -9,8 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "librswa.so")
-SOURCES = ["rswa_api.hip", "rswa_decode.hip", "rswa_masked.hip", "rswa_masked_bwd.hip",
-           "rswa_prefill.hip", "rswa_probe.hip"]
+SOURCES = ["rswa_api.hip", "rswa_decode.hip", "rswa_masked.hip", "rswa_masked_bwd.hip", "rswa_probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

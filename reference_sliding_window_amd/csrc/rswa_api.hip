@@ -329,30 +329,33 @@ rswa_status_t rswa_prefill(const rswa_cache_t *cache, const void *q, const void 
   if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return RSWA_ERR_ALIGN;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RSWA_ERR_ALIGN;
   if (!isfinite(scale)) return RSWA_ERR_SHAPE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (total_tokens > 0 && max_seq_len > 0) {
-    const rswa_status_t fs = rswa_masked_attn_varlen(
-        q, k, v, out, lse, cu_seqlens, cache->ref_len, cache->batch, total_tokens, max_seq_len,
-        cache->window, cache->num_heads, cache->head_dim, cache->dtype, prefix_mode, scale, stream);
-    if (fs != RSWA_OK) return fs;
-  }
-  HandoffParams hp{};
-  hp.k_src = k;
-  hp.v_src = v;
-  hp.cu_seqlens = cu_seqlens;
-  hp.k = cache->k;
-  hp.v = cache->v;
-  hp.seq_base = cache->seq_base;
-  hp.ref_len = cache->ref_len;
-  hp.step = cache->step;
-  hp.error = cache->error;
-  hp.batch = cache->batch;
-  hp.heads = cache->num_heads;
-  hp.window = cache->window;
-  hp.max_ref_len = cache->max_ref_len;
-  hp.total_tokens = total_tokens;
-  hp.max_seq_len = max_seq_len;
-  const hipError_t e = launch_handoff(hp, cache->dtype, cache->head_dim, s);
+  const int64_t qblocks = max_seq_len > 0 ? (max_seq_len + 127) / 128 : 1;
+  if ((int64_t)cache->batch * cache->num_heads * qblocks >= ((int64_t)1 << 31)) return RSWA_ERR_CAPACITY;
+  // One launch: the packed forward with the hand-off fused in (every sequence
+  // gets at least one workgroup per head, so empty samples still publish step[b]).
+  MaskedParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.cu_seqlens = cu_seqlens;
+  p.ref_lens = cache->ref_len;
+  p.num_seqs = cache->batch;
+  p.max_seq_len = max_seq_len;
+  p.seq_len = total_tokens;
+  p.window = cache->window;
+  p.heads = cache->num_heads;
+  p.prefix_mode = prefix_mode;
+  const float sc = scale == 0.f ? 1.f / sqrtf((float)cache->head_dim) : scale;
+  p.scale_log2 = sc * kLog2e;
+  p.cache_k = cache->k;
+  p.cache_v = cache->v;
+  p.seq_base = cache->seq_base;
+  p.step = cache->step;
+  p.error = cache->error;
+  p.max_ref_len = cache->max_ref_len;
+  const hipError_t e = launch_masked(p, cache->head_dim, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
 }
 

@@ -87,22 +87,16 @@ struct MaskedParams {
   int32_t num_seqs, max_seq_len;
   int32_t seq_len, ref_len, window, heads, prefix_mode;  // seq_len: total rows of the pack
   float scale_log2;
-};
-
-// Writes a prefilled pack into the cache: per sequence b (sample b of the pack),
-// the reference rows and the last min(n, T0) output rows into their slots, and
-// step[b] = T0 = rows - ref_len[b].
-struct HandoffParams {
-  const void *k_src;
-  const void *v_src;
-  const int32_t *cu_seqlens;
-  void *k;
-  void *v;
+  // Prefill hand-off (cache_k == nullptr: none). Sample b of the pack is cache
+  // sequence b, ref_lens is the cache's ref_len[] and window the cache's n: the
+  // reference rows and the last min(n, T0) output rows (T0 = rows - ref_len[b])
+  // are also written into their slots, and step[b] = T0.
+  void *cache_k;
+  void *cache_v;
   const int64_t *seq_base;
-  const int32_t *ref_len;
   int32_t *step;
   int32_t *error;
-  int32_t batch, heads, window, max_ref_len, total_tokens, max_seq_len;
+  int32_t max_ref_len;
 };
 
 struct MaskedBwdParams {
@@ -150,7 +144,6 @@ struct BwdPlan {
 BwdPlan plan_masked_bwd(int32_t seq_len, int32_t ref_len, int32_t heads, int32_t requested_parts);
 hipError_t launch_masked_bwd(const MaskedBwdParams &p, hipStream_t s);
 hipError_t launch_clear_word(int32_t *word, hipStream_t s);
-hipError_t launch_handoff(const HandoffParams &p, int32_t dtype, int32_t head_dim, hipStream_t s);
 hipError_t launch_probe_read(const void *buf, size_t bytes, float *sink, int32_t workgroups, hipStream_t s);
 
 }  // namespace rswa

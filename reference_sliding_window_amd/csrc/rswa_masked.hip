@@ -75,7 +75,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
   __shared__ Tile k_sm[2], v_sm[2];
   const int H = p.heads, n = p.window;
   const bool full_prefix = p.prefix_mode == RSWA_PREFIX_FULL;
-  const int nqb = (p.max_seq_len + kBM - 1) / kBM;
+  const int nqb = max(1, (p.max_seq_len + kBM - 1) / kBM);
   const int G = p.num_seqs * H * nqb;
   // XCD-aware order: logical work item w -> (head, sample, query block). An XCD
   // takes a contiguous range of w: the query blocks of one (sample, head) share
@@ -89,13 +89,30 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
   // One sample of the pack: rows [row0, row0 + N) with its own reference
   // length; no row sees another sample's keys.
   int row0 = 0, N = p.seq_len, Lm = p.ref_len;
+  bool handoff = false;
   if (p.cu_seqlens != nullptr) {
     row0 = p.cu_seqlens[sample];
     const int row1 = p.cu_seqlens[sample + 1];
     Lm = p.ref_lens[sample];
     N = row1 - row0;
+    const bool pack_bad = row0 < 0 || row1 < row0 || row1 > p.seq_len || N > p.max_seq_len || Lm > N;
+    if (p.cache_k != nullptr) {
+      // Prefill hand-off: the per-sequence checks of the cache calls; the
+      // first workgroup of the sequence publishes step[b] = T0 or the error.
+      int err = pack_bad ? RSWA_DEVERR_PACK : 0;
+      if (Lm < 0 || Lm > p.max_ref_len) err |= RSWA_DEVERR_REF_LEN;
+      const int64_t cb = p.seq_base[sample];
+      if (cb < 0 || (cb & 7) != 0) err |= RSWA_DEVERR_ALIGN;
+      if (w % nqb == 0 && h == 0 && threadIdx.x == 0) {
+        if (err != 0)
+          atomicOr(p.error, err);
+        else
+          p.step[sample] = N - Lm;
+      }
+      handoff = err == 0;
+    }
     // device-side metadata: a malformed sample is skipped
-    if (row0 < 0 || row1 < row0 || row1 > p.seq_len || N > p.max_seq_len || Lm < 0 || Lm > N) return;
+    if (pack_bad || Lm < 0) return;
   }
   if (q0 >= N) return;
   const int q_end = min(N, q0 + kBM);
@@ -282,6 +299,39 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
   }
   if (bi < nblocks) step(bi, std::integral_constant<int, 0>{}, sa, sb);
 
+  // Prefill hand-off: this workgroup's own rows [q0, q_end) of head h that the
+  // cache keeps -- reference row r -> slot r, output t = r - L_m + 1 among the
+  // last min(n, T0) -> slot L_m + ((t - 1) mod n) -- copied bit for bit. The
+  // workgroup has just streamed these rows, so they come from its XCD's L2.
+  if (handoff) {
+    const int keep_from = Lm + max(0, N - Lm - n);
+    const int64_t cb = p.seq_base[sample] + (int64_t)h * (Lm + n) * kD;
+    uint16_t *ck = static_cast<uint16_t *>(p.cache_k) + cb;
+    uint16_t *cv = static_cast<uint16_t *>(p.cache_v) + cb;
+    constexpr int kPer = kBM * (kD / 8) / (64 * kWaves);  // 16-byte chunks per thread and tensor
+    u32x4_t kx[kPer], vx[kPer];
+    int64_t dst[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = tid + j * 64 * kWaves;
+      const int r = q0 + i / (kD / 8), c = i % (kD / 8);
+      const bool keep = r < q_end && (r < Lm || r >= keep_from);
+      dst[j] = keep ? (int64_t)(r < Lm ? r : Lm + (r - Lm) % n) * kD + 8 * c : -1;
+      if (keep) {
+        const int64_t src = (int64_t)r * stride + 8 * c;
+        kx[j] = *reinterpret_cast<const u32x4_t *>(Kg + src);
+        vx[j] = *reinterpret_cast<const u32x4_t *>(Vg + src);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (dst[j] >= 0) {
+        *reinterpret_cast<u32x4_t *>(ck + dst[j]) = kx[j];
+        *reinterpret_cast<u32x4_t *>(cv + dst[j]) = vx[j];
+      }
+    }
+  }
+
   // Normalise and store: accumulator element r of o[db] is d = 32 db + 8 (r/4) + 4 hi + r%4.
   l = swap_halves_sum(l);
   if (!q_ok) return;
@@ -305,7 +355,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
 
 hipError_t launch_masked(const MaskedParams &p, int32_t head_dim, hipStream_t s) {
   if (head_dim != kD) return hipErrorInvalidValue;
-  const int nqb = (p.max_seq_len + kBM - 1) / kBM;
+  const int nqb = p.max_seq_len > 0 ? (p.max_seq_len + kBM - 1) / kBM : 1;
   const int64_t G = (int64_t)nqb * p.heads * p.num_seqs;
   if (G == 0) return hipSuccess;
   hipLaunchKernelGGL(masked_attn_kernel, dim3((unsigned)G), dim3(64 * kWaves), 0, s, p);

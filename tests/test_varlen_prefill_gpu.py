@@ -238,6 +238,66 @@ def test_prefill_flags_bad_sequences_and_keeps_the_rest():
     check_close(to_f64(out)[20:80], ref, "bf16", "good sequence of a pack with a bad one")
 
 
+
+def test_prefill_empty_pack_publishes_steps():
+    """No rows at all: sequences without a reference start at step 0; a sequence
+    whose reference does not fit its (empty) sample is flagged and keeps its state."""
+    n, H = 8, 2
+    banner("prefill of an empty pack")
+    cache = rs.KVCache.allocate([0, 0, 5], H, D, n, dtype=rs.RSWA_BF16)
+    cache.k.fill_(float("nan"))
+    cache.v.fill_(float("nan"))
+    cache.step.fill_(-5)
+    A = torch.zeros((16, H, D), dtype=torch.bfloat16, device="cuda")
+    rs.rswa_prefill(cache.desc, A, A, A, A, dev_i32([0, 0, 0, 0]), 0, 0, CAUSAL, 0.0)
+    torch.cuda.synchronize()
+    assert rs.rswa_check_device_error(cache.desc) == rs.RSWA_DEVERR_PACK
+    assert cache.step.cpu().tolist() == [0, 0, -5]
+    assert torch.isnan(cache.k.float()).all() and torch.isnan(cache.v.float()).all()
+
+
+def test_prefill_misaligned_sequence_is_flagged_and_skipped():
+    """A sequence whose cache block is not 16-byte aligned is flagged and left
+    untouched; its outputs are still computed, and the other sequences are handed
+    off as usual (prefix rows seeing the whole reference here)."""
+    refs, t0s, n, H = [16, 24, 8], [5, 20, 3], 8, 2
+    lens = [L + t for L, t in zip(refs, t0s)]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total = int(cu[-1])
+    banner(f"prefill with a misaligned sequence, refs={refs} t0s={t0s}")
+    Q, K, V = pack_tensors(total, H, 7800)
+    cache = rs.KVCache.allocate(refs, H, D, n, dtype=rs.RSWA_BF16)
+    cache.k.fill_(float("nan"))
+    cache.v.fill_(float("nan"))
+    cache.step.fill_(-5)
+    bases = list(cache._host_bases())
+    cache.seq_base[1] += 4  # 8 bytes off: not 16-byte aligned
+    out = torch.full((total, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    Qd, Kd, Vd = (to_dev(x, "bf16") for x in (Q, K, V))
+    rs.rswa_prefill(cache.desc, Qd, Kd, Vd, out, dev_i32(cu), total, max(lens), FULL, 0.0)
+    torch.cuda.synchronize()
+    assert rs.rswa_check_device_error(cache.desc) == rs.RSWA_DEVERR_ALIGN
+    assert cache.step.cpu().tolist() == [t0s[0], -5, t0s[2]]
+    got = to_f64(out)
+    for b, L in enumerate(refs):
+        ref, _ = sample_oracle(Q, K, V, cu[b], cu[b + 1], L, n, FULL)
+        check_close(got[cu[b]:cu[b + 1]], ref, "bf16", f"sequence {b} outputs")
+    kbits, vbits = bits(cache.k), bits(cache.v)
+    size1 = H * (refs[1] + n) * D
+    assert np.all(kbits[bases[1]:bases[1] + size1] == 0x7FC0), "misaligned sequence written"
+    assert np.all(vbits[bases[1]:bases[1] + size1] == 0x7FC0), "misaligned sequence written"
+    for b in (0, 2):
+        L, t0 = refs[b], t0s[b]
+        blk_k = kbits[bases[b]:bases[b] + H * (L + n) * D].reshape(H, L + n, D)
+        blk_v = vbits[bases[b]:bases[b] + H * (L + n) * D].reshape(H, L + n, D)
+        for slot, pos in enumerate(orc.ring_image(L, n, t0)):
+            if pos == 0:
+                assert np.all(blk_k[:, slot] == 0x7FC0), f"seq {b} slot {slot} written"
+                continue
+            row = cu[b] + pos - 1
+            assert np.array_equal(blk_k[:, slot], K[row]), f"seq {b} slot {slot} K"
+            assert np.array_equal(blk_v[:, slot], V[row]), f"seq {b} slot {slot} V"
+
 @pytest.mark.slow
 @pytest.mark.parametrize("t0", [128, 200])
 def test_prefill_40page_full_size(t0):
