@@ -326,6 +326,23 @@ def _ring_slot_off_by_one(L_m, n, T):
     return L_m + T % n
 
 
+_true_columns = orc.masked_visible_columns
+
+
+def _columns_without_diagonal(i, L_m, n, prefix_mode=orc.PREFIX_CAUSAL):
+    return [j for j in _true_columns(i, L_m, n, prefix_mode) if j != i]
+
+
+def _causal_prefix_sees_whole_prefix(i, L_m, n, prefix_mode=orc.PREFIX_CAUSAL):
+    return list(range(L_m)) if i < L_m else _true_columns(i, L_m, n, prefix_mode)
+
+
+def _output_rows_one_step_early(i, L_m, n, prefix_mode=orc.PREFIX_CAUSAL):
+    if i < L_m:
+        return _true_columns(i, L_m, n, prefix_mode)
+    return [p - 1 for p in orc.visible_positions(L_m, n, i - L_m + 1)]
+
+
 MUTANTS = [
     ("decode_window", _window_too_narrow),
     ("decode_window", _window_too_wide),
@@ -335,6 +352,9 @@ MUTANTS = [
     ("attend", _attend_k_v_swapped),
     ("attend", _attend_unnormalised),
     ("ring_slot", _ring_slot_off_by_one),
+    ("masked_visible_columns", _columns_without_diagonal),
+    ("masked_visible_columns", _causal_prefix_sees_whole_prefix),
+    ("masked_visible_columns", _output_rows_one_step_early),
 ]
 
 
