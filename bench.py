@@ -273,6 +273,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     rs.library()  # fail loudly if the HIP library is missing
+    # secondary lines draw their timing inputs on the device from torch's seeded generator
+    torch.manual_seed(wl.FORTY_PAGE.base_seed)
 
     if args.copy_reference:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
