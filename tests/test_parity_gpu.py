@@ -367,6 +367,9 @@ def _masked_case(N, L_m, n, H, mode, seed):
     (513, 130, 128, rs.RSWA_PREFIX_CAUSAL),
     (640, 97, 1, rs.RSWA_PREFIX_CAUSAL),
     (700, 300, 200, rs.RSWA_PREFIX_FULL),
+    (1, 0, 1, rs.RSWA_PREFIX_CAUSAL),
+    (161, 33, 1000, rs.RSWA_PREFIX_CAUSAL),
+    (200, 200, 4, rs.RSWA_PREFIX_CAUSAL),
 ])
 def test_masked_small_every_row(N, L_m, n, mode):
     H = 2
