@@ -215,3 +215,67 @@ def test_prefill_random_cache_images(case):
                 continue
             assert np.array_equal(blk_k[:, slot], K[r0 + pos - 1]), f"seq {b} slot {slot} K"
             assert np.array_equal(blk_v[:, slot], V[r0 + pos - 1]), f"seq {b} slot {slot} V"
+
+
+def decode_cases(count, seed):
+    g = np.random.default_rng(seed)
+    cases = []
+    for _ in range(count):
+        B, H = int(g.integers(1, 5)), int(g.integers(1, 4))
+        n = int(g.choice([1, 2, 7, 16, 64, 128, 129, 300]))
+        cases.append((B, H, int(g.choice([64, 128])), str(g.choice(["bf16", "fp32"])),
+                      [int(x) for x in g.integers(0, 300, B)], n, int(g.integers(1, min(80, 2 * n + 4) + 1)),
+                      int(g.choice([0, 1, 3, 8]))))
+    return cases
+
+
+@pytest.mark.parametrize("case", decode_cases(12, 2030),
+                         ids=lambda c: "B%d-H%d-d%d-%s-n%d-T%d-s%d" % (c[0], c[1], c[2], c[3], c[5], c[6], c[7]))
+def test_decode_random_every_step_and_cache_image(case):
+    """Per-sequence reference lengths, fused append + attend from an empty window
+    through wrap-around, every step against the oracle; then the cache bit for bit."""
+    B, H, d, dt, refs, n, steps, splits = case
+    code = rs.RSWA_BF16 if dt == "bf16" else rs.RSWA_FP32
+    banner(f"random decode B={B} H={H} d={d} {dt} refs={refs} n={n} steps={steps} splits={splits}")
+    seed = 9500 + sum(refs) + steps
+    kref = [wl.draw(dt, 1.0, (H, L, d), seed, 0, b) for b, L in enumerate(refs)]
+    vref = [wl.draw(dt, 1.0, (H, L, d), seed, 1, b) for b, L in enumerate(refs)]
+    bases = np.concatenate([[0], np.cumsum([H * L * d for L in refs])[:-1]]).astype(np.int64)
+    flat = lambda xs: np.concatenate([x.reshape(-1) for x in xs] + [np.zeros(8, xs[0].dtype)])
+    cache = rs.KVCache.allocate(refs, H, d, n, dtype=code)
+    rs.rswa_cache_init(cache.desc, to_dev(flat(kref), dt), to_dev(flat(vref), dt),
+                       torch.tensor(bases, dtype=torch.int64, device="cuda"))
+    ws = cache.workspace(splits)
+    out = torch.empty((B, H, d), dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device="cuda")
+    new = [[wl.draw(dt, 1.0, (B, H, d), seed, tid, T) for T in range(1, steps + 1)] for tid in (2, 3, 4)]
+    f = lambda a: wl.to_f64(a, dt)
+    for T in range(1, steps + 1):
+        q, k, v = (to_dev(x[T - 1], dt) for x in new)
+        rs.rswa_decode_attn(cache.desc, q, out, k, v, 0.0, splits, ws)
+        got = to_f64(out)
+        ref = np.empty_like(got)
+        for b, L in enumerate(refs):
+            ok = np.stack([new[1][t][b] for t in range(T)])  # outputs 1..T, [T][H][d]
+            ov = np.stack([new[2][t][b] for t in range(T)])
+            for h in range(H):
+                ref[b, h] = orc.decode_output(f(new[0][T - 1][b, h]), f(kref[b][h]), f(vref[b][h]),
+                                              f(ok[:, h]), f(ov[:, h]), 1, L, n, T, 1.0 / np.sqrt(d))
+        check_close(got, ref, dt, f"decode step {T}")
+    torch.cuda.synchronize()
+    assert rs.rswa_check_device_error(cache.desc) == 0
+    assert cache.step.cpu().tolist() == [steps] * B
+    kbits, vbits = bits(cache.k), bits(cache.v)
+    sb = lambda a: a.view(np.uint16) if dt == "bf16" else a.view(np.uint32)
+    for b, L in enumerate(refs):
+        base = cache._host_bases()[b]
+        blk_k = kbits[base:base + H * (L + n) * d].reshape(H, L + n, d)
+        blk_v = vbits[base:base + H * (L + n) * d].reshape(H, L + n, d)
+        for slot, pos in enumerate(orc.ring_image(L, n, steps)):
+            if pos == 0:
+                continue  # never written: the pool was not initialised
+            if pos <= L:
+                want_k, want_v = kref[b][:, pos - 1], vref[b][:, pos - 1]
+            else:
+                want_k, want_v = new[1][pos - L - 1][b], new[2][pos - L - 1][b]
+            assert np.array_equal(blk_k[:, slot], sb(want_k)), f"seq {b} slot {slot} K"
+            assert np.array_equal(blk_v[:, slot], sb(want_v)), f"seq {b} slot {slot} V"
