@@ -346,7 +346,7 @@ def main():
         "hbm_frac_of_peak": achieved / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "rswa decode step (split-K attention + split merge), one call",
+                     "kernel": "rswa decode step (split-K attention, merged in the same launch when the plan has one chunk per (sequence, head)), one call",
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "achievable_read_GBps": achievable, "frac_of_achievable": achieved / achievable},
         "device": device_facts(torch),

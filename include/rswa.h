@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RSWA_ABI_VERSION 5
+#define RSWA_ABI_VERSION 6
 
 #if defined(__GNUC__)
 #define RSWA_API __attribute__((visibility("default")))
@@ -107,6 +107,7 @@ typedef struct rswa_cache {
   const int32_t *ref_len;  /* device [B], L_m per sequence                        */
   int32_t *step;           /* device [B], T per sequence                          */
   int32_t *error;          /* device, one int32 word of RSWA_DEVERR_* bits        */
+  int32_t *arrive;         /* NULL, or device [B] arrival counters (see below)    */
 } rswa_cache_t;
 
 /* Library ABI version (RSWA_ABI_VERSION). */
@@ -117,7 +118,8 @@ RSWA_API const char *rswa_status_str(int32_t status);
 
 /*
  * Write the reference segment into the cache ("encoded once, never updated":
- * 夜雨聆风 page, same section as above) and reset step[b] = 0 for every b.
+ * 夜雨聆风 page, same section as above) and reset step[b] = 0 (and arrive[b] = 0
+ * when arrive is set) for every b.
  * k_ref, v_ref: device; sequence b's reference at element offset ref_base[b]
  * (device [B]), laid out [H][ref_len[b]][head_dim], same dtype as the cache.
  * When max_ref_len == 0 the three may be NULL. Does not touch the window slots.
@@ -162,6 +164,15 @@ RSWA_API size_t rswa_decode_workspace_size(const rswa_cache_t *cache, int32_t nu
  *
  * Accumulation is fp32. Softmax runs in base 2 with log2(e) folded into the
  * scale.
+ *
+ * Launches: with more than one split, a split kernel and a merge kernel. With
+ * one split the split kernel writes out itself (one launch); a fused call then
+ * also needs cache->arrive (otherwise it keeps the merge launch): the H
+ * workgroups of sequence b count their arrival in arrive[b], and the last one
+ * publishes step[b] and sets arrive[b] back to 0. arrive must hold zeros before
+ * the first call (rswa_cache_init zeroes it) and is zero again after every
+ * call. The library picks one split when every sequence fits one chunk of a
+ * batch that fills the GPU.
  */
 RSWA_API rswa_status_t rswa_decode_attn(const rswa_cache_t *cache, const void *q, void *out,
                                const void *k_new, const void *v_new, float scale,
@@ -221,7 +232,8 @@ RSWA_API rswa_status_t rswa_masked_attn_varlen(const void *q, const void *k, con
  * with window = cache->window, out and lse as there) and leaves the cache as
  * rswa_cache_init followed by T0_b appends would: reference rows in slots
  * 0 .. ref_len[b]-1, the last min(window, T0_b) outputs in their ring slots
- * ref_len[b] + ((t-1) mod window), step[b] = T0_b (yhxrc and 夜雨聆风 pages;
+ * ref_len[b] + ((t-1) mod window), step[b] = T0_b, arrive[b] = 0 when
+ * arrive is set (yhxrc and 夜雨聆风 pages;
  * WeThinkIn page, Eq. (6)). Decode then continues with output T0_b + 1.
  *  q, k, v, out  device [total_tokens][num_heads][head_dim], cache dtype; only
  *                RSWA_BF16 with head_dim 128 (the packed kernel's case). k and v

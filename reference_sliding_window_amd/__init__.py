@@ -70,6 +70,7 @@ class CacheDesc(ctypes.Structure):
         ("ref_len", ctypes.c_void_p),
         ("step", ctypes.c_void_p),
         ("error", ctypes.c_void_p),
+        ("arrive", ctypes.c_void_p),
     ]
 
 
@@ -330,6 +331,7 @@ class KVCache:
     ref_len: torch.Tensor
     step: torch.Tensor
     error: torch.Tensor
+    arrive: torch.Tensor
     ref_lens: list
     window: int
     heads: int
@@ -352,10 +354,11 @@ class KVCache:
         ref_len = torch.tensor(ref_lens, dtype=torch.int32, device=device)
         step = torch.zeros(len(ref_lens), dtype=torch.int32, device=device)
         error = torch.zeros(4, dtype=torch.int32, device=device)
+        arrive = torch.zeros(len(ref_lens), dtype=torch.int32, device=device)  # zero before first use
         desc = CacheDesc(len(ref_lens), heads, head_dim, window, max(ref_lens), dtype,
                          k.data_ptr(), v.data_ptr(), seq_base.data_ptr(), ref_len.data_ptr(),
-                         step.data_ptr(), error.data_ptr())
-        return KVCache(desc, k, v, seq_base, ref_len, step, error, ref_lens, window, heads, head_dim)
+                         step.data_ptr(), error.data_ptr(), arrive.data_ptr())
+        return KVCache(desc, k, v, seq_base, ref_len, step, error, arrive, ref_lens, window, heads, head_dim)
 
     def block(self, pool: torch.Tensor, b: int) -> torch.Tensor:
         """View of sequence b's [H][L_m + n][d] block of a pool."""

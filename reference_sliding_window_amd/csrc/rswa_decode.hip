@@ -82,6 +82,17 @@ struct F32 {
   }
 };
 
+// Stores one fp32 result into an output of the cache dtype (bf16: round to
+// nearest even).
+template <class E>
+__device__ inline void store_out(void *out, int64_t i, float o) {
+  if constexpr (E::kBytes == 2) {
+    static_cast<uint16_t *>(out)[i] = Bf16::round(o);
+  } else {
+    static_cast<float *>(out)[i] = o;
+  }
+}
+
 // ------------------------------------------------------------ lane reductions
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
@@ -146,7 +157,10 @@ __global__ __launch_bounds__(256) void cache_init_kernel(InitParams p) {
     if (blockIdx.x == 0 && h == 0 && threadIdx.x == 0) atomicOr(p.error, err);
     return;
   }
-  if (blockIdx.x == 0 && h == 0 && threadIdx.x == 0) p.step[b] = 0;
+  if (blockIdx.x == 0 && h == 0 && threadIdx.x == 0) {
+    p.step[b] = 0;
+    if (p.arrive != nullptr) p.arrive[b] = 0;
+  }
   const int r0 = blockIdx.x * kRows;
   const int r1 = min(L, r0 + kRows);
   if (r0 >= r1) return;
@@ -238,7 +252,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 
   const int start = sp * p.chunk;
   const int end = min(vis, start + p.chunk);
-  if (err || start >= end) {  // empty partial state
+  if (err || start >= end) {  // empty partial state (one launch: a zero output)
+    if (p.one_launch) {
+      for (int i = threadIdx.x; i < D; i += 256) store_out<E>(p.out, bh * D + i, 0.f);
+      return;
+    }
     for (int i = threadIdx.x; i < D; i += 256) po[i] = 0.f;
     if (threadIdx.x == 0) {
       pml[0] = kNegInf;
@@ -362,10 +380,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
       o = fmaf(a, sm_acc[w2][threadIdx.x], o);
       lsum = fmaf(a, sm_l[w2], lsum);
     }
-    po[threadIdx.x] = o;
-    if (threadIdx.x == 0) {
-      pml[0] = M;
-      pml[1] = lsum;
+    if (p.one_launch) {
+      store_out<E>(p.out, bh * D + threadIdx.x, o / lsum);  // what the merge of one split computes
+    } else {
+      po[threadIdx.x] = o;
+      if (threadIdx.x == 0) {
+        pml[0] = M;
+        pml[1] = lsum;
+      }
+    }
+  }
+  // One fused launch: every workgroup of sequence b read step[b] before it
+  // counts itself here, so the last of the H may publish the new step.
+  if (p.one_launch && fused && threadIdx.x == 0) {
+    if (atomicAdd(&p.arrive[b], 1) == p.heads - 1) {
+      atomicExch(&p.arrive[b], 0);
+      p.step[b] = T0 + 1;
     }
   }
 }
@@ -390,13 +420,7 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
     }
     o = num / den;
   }
-  using S = typename E::storage;
-  S *out = static_cast<S *>(p.out) + bh * D;
-  if constexpr (E::kBytes == 2) {
-    out[col] = Bf16::round(o);
-  } else {
-    out[col] = o;
-  }
+  store_out<E>(p.out, bh * D + col, o);
   if (h == 0 && col == 0 && p.k_new != nullptr) {
     const int32_t next = p.seq_state[b];
     if (next >= 0) p.step[b] = next;
@@ -414,7 +438,7 @@ hipError_t launch_decode_t(const DecodeParams &p, hipStream_t s) {
   dim3 grid(p.heads, p.batch, p.splits);
   hipLaunchKernelGGL((decode_split_kernel<E, D, kU>), grid, dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.one_launch) return e;
   hipLaunchKernelGGL((decode_merge_kernel<E, D>), dim3(p.heads, p.batch), dim3(D), 0, s, p);
   return hipGetLastError();
 }

@@ -43,6 +43,11 @@ struct DecodeParams {
   float *part_o;
   float *part_ml;
   int32_t *seq_state;
+  // One launch (splits == 1 and, for a fused call, arrival counters given): the
+  // split kernel writes out itself; the last of a sequence's H workgroups to
+  // count itself in arrive[b] publishes step[b] and sets arrive[b] back to 0.
+  int32_t *arrive;
+  int32_t one_launch;
   int32_t batch, heads, window, max_ref_len;
   int32_t splits, chunk;
   float scale_log2;  // softmax scale * log2(e)
@@ -71,6 +76,7 @@ struct InitParams {
   const int32_t *ref_len;
   int32_t *step;
   int32_t *error;
+  int32_t *arrive;  // nullable
   int32_t batch, heads, window, max_ref_len;
 };
 
@@ -96,6 +102,7 @@ struct MaskedParams {
   const int64_t *seq_base;
   int32_t *step;
   int32_t *error;
+  int32_t *arrive;  // nullable: the cache's decode arrival counters, reset with step
   int32_t max_ref_len;
 };
 

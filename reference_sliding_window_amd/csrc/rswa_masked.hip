@@ -104,10 +104,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
       const int64_t cb = p.seq_base[sample];
       if (cb < 0 || (cb & 7) != 0) err |= RSWA_DEVERR_ALIGN;
       if (w % nqb == 0 && h == 0 && threadIdx.x == 0) {
-        if (err != 0)
+        if (err != 0) {
           atomicOr(p.error, err);
-        else
+        } else {
           p.step[sample] = N - Lm;
+          if (p.arrive != nullptr) p.arrive[sample] = 0;
+        }
       }
       handoff = err == 0;
     }

@@ -69,6 +69,7 @@ def good_desc(**kw):
     ("step", None, rs.RSWA_ERR_NULL),
     ("error", None, rs.RSWA_ERR_NULL),
     ("v", A + 8, rs.RSWA_ERR_ALIGN),
+    ("arrive", A + 2, rs.RSWA_ERR_ALIGN),
 ])
 def test_bad_descriptor_rejected_by_every_cache_call(field, value, status):
     desc = good_desc(**{field: value})
@@ -105,6 +106,20 @@ def test_workspace_grows_with_splits():
     assert 0 < s1 < s16
     # 16 splits: 32*16*16 partial states of 128 floats plus (max, sum) pairs
     assert s16 >= 32 * 16 * 16 * (128 + 2) * 4
+
+
+def test_library_split_choice():
+    """One chunk per (sequence, head) -- one launch -- for a batch that fills the GPU with
+    sequences of at most 12288 slots; split chunks otherwise."""
+    ws = lambda s, **kw: rs.rswa_decode_workspace_size(good_desc(**kw), s)
+    forty = dict(batch=32, num_heads=16, max_ref_len=10272, window=128)
+    assert ws(0, **forty) == ws(1, **forty)
+    one_page = dict(batch=1, num_heads=16, max_ref_len=288, window=128)
+    assert ws(0, **one_page) > ws(1, **one_page)
+    ragged = dict(batch=64, num_heads=16, max_ref_len=12832, window=128)
+    assert ws(0, **ragged) == ws(4, **ragged)
+    few = dict(batch=2, num_heads=16, max_ref_len=10272, window=128)
+    assert ws(0, **few) > ws(8, **few)
 
 
 def test_append_and_init_argument_checks():

@@ -191,6 +191,30 @@ def test_split_count_invariance(splits):
         check_close(o.reshape(-1, 128), run.oracle(T), "fp32", f"splits={splits} T={T}")
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 64)])
+def test_one_launch_equals_split_and_merge(dtype, d):
+    """With one split, the single launch (arrival counters given) and the split + merge
+    launches (no counters) give the same bits, step counts and cache images, through
+    the wrap; the counters are back at zero after every call."""
+    B, H, L, n, steps = 3, 4, 150, 16, 40
+    w = wl.DecodeWorkload("one-launch", batch=B, heads=H, head_dim=d, ref_len=L, window=n, steps=steps,
+                          dtype=dtype, sigma_q=1.0, sigma_kv=1.0, base_seed=78)
+    banner(f"one launch vs split + merge {dtype} d={d}")
+    one, two = DecodeRun(w, num_splits=1), DecodeRun(w, num_splits=1)
+    two.cache.desc.arrive = None
+    for T in range(1, steps + 1):
+        q, k, v = (to_dev(x[0], dtype) for x in wl.steps_qkv(w, T, T))
+        for r in (one, two):
+            rs.rswa_decode_attn(r.cache.desc, q, r.out, k, v, 0.0, 1, r.ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(one.out), bits(two.out)), f"step {T}"
+        assert one.cache.arrive.cpu().tolist() == [0] * B
+    assert one.cache.step.cpu().tolist() == two.cache.step.cpu().tolist() == [steps] * B
+    assert np.array_equal(bits(one.cache.k), bits(two.cache.k))
+    assert np.array_equal(bits(one.cache.v), bits(two.cache.v))
+    assert rs.rswa_check_device_error(one.cache.desc) == 0
+
+
 @pytest.mark.parametrize("L_m,n,d", [(0, 4, 64), (1, 1, 128), (3, 2, 64), (130, 128, 128), (64, 300, 64)])
 def test_decode_shapes_fp32(L_m, n, d):
     w = _small_fp32(L_m=L_m, n=n, d=d, steps=2 * n + 5 if n < 100 else 140)
