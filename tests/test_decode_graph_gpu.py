@@ -39,9 +39,18 @@ def make_layers(refs, H, d, n, L, dtype, seed):
     return caches, kref
 
 
-@pytest.mark.parametrize("dtype,d", [(rs.RSWA_BF16, 128), (rs.RSWA_FP32, 64)])
-def test_graph_replays_equal_eager_steps(dtype, d):
-    refs, H, n, L, steps = [40, 0, 77], 2, 8, 3, 20
+FULL_BATCH = [int(x) for x in np.random.default_rng(8099).integers(0, 120, 32)]
+
+
+@pytest.mark.parametrize("dtype,d,refs,H", [
+    (rs.RSWA_BF16, 128, [40, 0, 77], 2),
+    (rs.RSWA_FP32, 64, [40, 0, 77], 2),
+    # B * H = 512 short sequences: the library decodes in one launch per layer (one chunk per
+    # sequence and head, steps published through the arrival counters)
+    (rs.RSWA_BF16, 128, FULL_BATCH, 16),
+], ids=["bf16-d128", "fp32-d64", "bf16-one-launch"])
+def test_graph_replays_equal_eager_steps(dtype, d, refs, H):
+    n, L, steps = 8, 3, 20
     B = len(refs)
     tdt = "bf16" if dtype == rs.RSWA_BF16 else "fp32"
     tt = torch.bfloat16 if dtype == rs.RSWA_BF16 else torch.float32
@@ -75,6 +84,7 @@ def test_graph_replays_equal_eager_steps(dtype, d):
             hist.append([to_f64(sout[0]).copy()])
         for l in range(L):
             assert graphed[l].step.cpu().tolist() == [steps] * B
+            assert graphed[l].arrive.cpu().tolist() == [0] * B
             assert rs.rswa_check_device_error(graphed[l].desc) == 0
         # layer 0 against the oracle's queue model, every step, every (sequence, head)
         f = lambda a: wl.to_f64(a, tdt)
