@@ -30,6 +30,9 @@
  *    by rswa_check_device_error.
  *  - Tensors of element type rswa_dtype_t; bf16 means IEEE bfloat16 bit
  *    patterns. All pointers must be 16-byte aligned.
+ *  - Calls that use the same cache or the same workspace must be ordered (one
+ *    stream, or events between streams): their device state (step, arrive,
+ *    window slots, partial results) is read and written without locks.
  *  - Nothing is thrown across the ABI and nothing aborts.
  */
 #ifndef RSWA_H
