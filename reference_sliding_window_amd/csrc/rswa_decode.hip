@@ -9,7 +9,10 @@
 //     over N(t) = P ∪ D_n(t) (WeThinkIn "Unlimited OCR Works：一篇读懂 R-SWA…",
 //     section 方法展开.3, Eqs. (1)-(4)); with the ring layout N(t) is the
 //     contiguous slot range [0, L_m + min(n, T)) (Eq. (6));
-//   * split merge       -- combines the per-chunk softmax states.
+//   * split merge       -- combines the per-chunk softmax states; with a
+//     single chunk per (sequence, head) the split kernel writes the output
+//     itself and the last of a sequence's workgroups publishes its step
+//     through the cache's arrival counter (one launch per step).
 //
 // Memory-bound design: each K/V row of d bf16 values (256 B at d = 128) is
 // read by 16 lanes with one 16-byte load each, so a wave64 load instruction
