@@ -50,13 +50,14 @@ bool verbose() {
 SplitPlan plan_decode_splits(int32_t batch, int32_t heads, int32_t max_len, int32_t requested) {
   // Default: about 4 workgroups per CU (1024 over the 256 CUs) -- where a plain
   // non-temporal read stream peaks on MI355X -- but never chunks below 64 slots,
-  // and never above 4096: per-sequence lengths live on the device, and in a
+  // and never above 2048: per-sequence lengths live on the device, and in a
   // ragged batch a cap on the chunk keeps one long sequence from becoming one
-  // long workgroup (measured: 64 sequences of 289..12960 slots, 0.58 -> 0.51 ms;
-  // the uniform 40-page batch is unchanged).
+  // long workgroup (measured: 64 sequences of 289..12960 slots, 0.58 ms with no
+  // cap, 0.51 ms with 4096, 0.50 ms with 2048; a batch of 32 sequences of 16416
+  // slots 624 -> 627 us with 2048; 4 sequences of 10400 slots unchanged).
   constexpr int64_t kTargetWorkgroups = 1024;
   constexpr int32_t kMinChunk = 64;
-  constexpr int32_t kMaxChunk = 4096;
+  constexpr int32_t kMaxChunk = 2048;
   const int64_t bh = (int64_t)batch * heads;
   const int32_t len = max_len > 0 ? max_len : 1;
   // One workgroup per (sequence, head), written out without a merge launch,
