@@ -96,6 +96,11 @@ typedef enum { RSWA_PREFIX_CAUSAL = 0, RSWA_PREFIX_FULL = 1 } rswa_prefix_mode_t
  *
  * step[b] is T, the number of outputs appended so far. It lives on the device
  * so that decode steps need no host synchronisation.
+ *
+ * arrive (optional, ABI 6) is device int32 [B] of arrival counters that let a
+ * fused decode step run as one launch (see rswa_decode_attn). It must hold
+ * zeros before the first decode call; rswa_cache_init and rswa_prefill zero
+ * it, and every decode call leaves it zero. NULL keeps the two-launch path.
  */
 typedef struct rswa_cache {
   int32_t batch;        /* B >= 1                                                 */
