@@ -346,6 +346,35 @@ def test_device_error_flags():
     assert int(cache.step[1].item()) == 2                        # the valid sequence advanced
 
 
+def test_one_launch_device_errors_leave_counters_at_zero():
+    """A full batch decoded in one launch: sequences with invalid device state are
+    flagged, keep their step, get zero outputs, and never count themselves in; the
+    other sequences advance and every arrival counter is back at zero."""
+    B, H, d, n, L = 32, 16, 128, 8, 40
+    banner("one-launch decode with flagged sequences")
+    cache = rs.KVCache.allocate([L] * B, H, d, n, dtype=rs.RSWA_BF16)
+    cache.k.normal_()
+    cache.v.normal_()
+    ws = cache.workspace()
+    assert ws.numel() == rs.rswa_decode_workspace_size(cache.desc, 1)  # one chunk per (sequence, head)
+    q, k, v = (torch.randn((B, H, d), device="cuda").to(torch.bfloat16) for _ in range(3))
+    out = torch.empty_like(q)
+    cache.ref_len[3] = L + 1   # above max_ref_len
+    cache.step[7] = -2
+    for _ in range(3):
+        rs.rswa_decode_attn(cache.desc, q, out, k, v, 0.0, 0, ws)
+    torch.cuda.synchronize()
+    flags = rs.rswa_check_device_error(cache.desc)
+    assert flags & rs.RSWA_DEVERR_REF_LEN and flags & rs.RSWA_DEVERR_STEP
+    steps = cache.step.cpu().tolist()
+    assert steps[3] == 0 and steps[7] == -2
+    assert all(t == 3 for b, t in enumerate(steps) if b not in (3, 7))
+    assert cache.arrive.cpu().tolist() == [0] * B
+    o = out.float()
+    assert torch.all(o[3] == 0) and torch.all(o[7] == 0)
+    assert torch.isfinite(o).all()
+
+
 def test_active_mask_and_guard_regions():
     """Sequences with active[b] = 0 are untouched; nothing is written outside the blocks."""
     banner("active mask and canary guards")
