@@ -5,7 +5,8 @@ Gradient tolerance: the gradients are bf16 outputs whose size grows with the
 number of terms summed (a prefix key's dK/dV gathers every row that sees it),
 and the kernels round P and dS to bf16 as matrix-core operands, so the error is
 relative to the gradient's magnitude: max|diff| <= 2e-2 * max(1, max|ref|) and
-||diff||_2 / ||ref||_2 <= 1e-2. The log-sum-exp is fp32, but the forward sums
+||diff||_2 / ||ref||_2 <= 1e-2, over each gradient tensor and for each key or
+row vector of each head (see gpu_util.check_grad). The log-sum-exp is fp32, but the forward sums
 the probabilities it has rounded to bf16 (each within 2^-9 relative), so its
 normaliser is within a factor 1 +- 2^-9 of the exact one:
 |diff| <= 2^-9 + 2e-4 + 1e-5 |ref| (the rest covers fp32 scores and exp2)."""
@@ -15,10 +16,11 @@ import numpy as np
 import pytest
 import torch
 
+import oracle.pool as opool
 import oracle.rswa as orc
 import reference_sliding_window_amd as rs
 import workloads as wl
-from gpu_util import check_close, to_dev, to_f64
+from gpu_util import check_close, check_grad, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -27,19 +29,6 @@ CAUSAL, FULL = rs.RSWA_PREFIX_CAUSAL, rs.RSWA_PREFIX_FULL
 
 def banner(msg):
     print(f"\n[case] {msg}", flush=True)
-
-
-def check_grad(got, ref, what):
-    d = got - ref
-    scale = max(1.0, float(np.abs(ref).max()) if ref.size else 1.0)
-    maxabs = float(np.abs(d).max()) if d.size else 0.0
-    rel = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300))
-    assert np.isfinite(got).all(), f"{what}: non-finite output"
-    if np.linalg.norm(ref) == 0.0:  # e.g. one visible key: dS = 0 exactly
-        rel = 0.0
-    assert maxabs <= 2e-2 * scale and rel <= 1e-2, \
-        f"{what}: max|d|={maxabs:.3e} (<= {2e-2 * scale:.3e}) rel={rel:.3e} (<= 1e-2)"
-    return maxabs, rel
 
 
 class PackedRun:
@@ -246,6 +235,56 @@ def test_backward_32k_sampled_and_column_sums(mode):
     worst = float((np.abs(dk_sum) / bound).max())
     print(f"sum_j dK_j: max |sum| = {np.abs(dk_sum).max():.3e}, worst |sum| / bound = {worst:.3f}")
     assert worst <= 1.0, f"sum_j dK_j exceeds 2^-9 sum_j |dK_j| (ratio {worst:.3f})"
+
+
+@pytest.mark.slow
+def test_backward_32k_reference_keys_elementwise():
+    """The library's default plan at 32K cuts each reference key's walk over the
+    query rows into 4 runs whose fp32 partials the reduction kernel adds. Here dK
+    and dV of reference keys at the segment's edges, its middle and 5 seeded
+    positions are compared element by element, heads 0 and H-1, both prefix
+    modes, against the oracle's backward over every row that sees them (on all
+    host cores). Output rows see the same keys in both modes, so their
+    contributions are computed once and the prefix rows' per mode."""
+    mw = wl.PACKED_32K
+    N, L_m, n, H = mw.seq_len, mw.ref_len, mw.window, mw.heads
+    default = rs.rswa_masked_bwd_workspace_size(N, L_m, H, 0)
+    assert default == rs.rswa_masked_bwd_workspace_size(N, L_m, H, 4) != \
+        rs.rswa_masked_bwd_workspace_size(N, L_m, H, 1), "the default plan at 32K is 4 runs"
+    rng = np.random.default_rng(13)
+    keys = sorted(set([0, 1, 127, 128, L_m // 2, L_m - 2, L_m - 1] +
+                      rng.integers(2, L_m - 2, 5).tolist()))
+    hs = [0, H - 1]
+    got = {}
+    for mode in (CAUSAL, FULL):
+        banner(f"packed 32K bwd, default plan, reference keys {keys}, heads {hs}, mode={mode}")
+        r = PackedRun(N, L_m, n, H, mode, seed=mw.base_seed, sigma=mw.sigma)
+        r.forward()
+        r.backward()
+        torch.cuda.synchronize()
+        got[mode] = (to_f64(r.dk)[keys][:, hs], to_f64(r.dv)[keys][:, hs])
+        inputs = (r.Q, r.K, r.V, r.G)
+        del r
+    print(f"oracle: {N} rows x {len(hs)} heads on {opool.workers()} processes", flush=True)
+    out_rows = list(range(L_m, N))
+    pre_rows = list(range(L_m))
+    with opool.SharedArrays() as arrays:
+        for name, a in zip(("Q", "K", "V", "dO"), inputs):
+            arrays.put(name, wl.bf16_bits_to_f32(a))   # exact values of the bf16 inputs
+        tasks = [(out_rows[i::96], keys, hs, L_m, n, mw.scale, CAUSAL) for i in range(96)]
+        for mode in (CAUSAL, FULL):
+            tasks += [(pre_rows[i::16], keys, hs, L_m, n, mw.scale, mode) for i in range(16)]
+        parts = opool.pool_map(opool.masked_bwd_keys_job, tasks, arrays)
+    out_dk = sum(p[0] for p in parts[:96])
+    out_dv = sum(p[1] for p in parts[:96])
+    for k, mode in enumerate((CAUSAL, FULL)):
+        pre = parts[96 + 16 * k:96 + 16 * (k + 1)]
+        ref_dk = out_dk + sum(p[0] for p in pre)
+        ref_dv = out_dv + sum(p[1] for p in pre)
+        ma, rel = check_grad(got[mode][0], ref_dk, f"dK reference keys, mode {mode}")
+        print(f"mode {mode} dK: max|d|={ma:.3e} worst (key, head) rel={rel:.3e}")
+        ma, rel = check_grad(got[mode][1], ref_dv, f"dV reference keys, mode {mode}")
+        print(f"mode {mode} dV: max|d|={ma:.3e} worst (key, head) rel={rel:.3e}")
 
 
 class _RowView:

@@ -15,7 +15,9 @@ import torch
 import oracle.rswa as orc
 import reference_sliding_window_amd as rs
 import workloads as wl
-from gpu_util import DecodeRun, bits, check_close, storage_bits, to_dev, to_f64
+import oracle.pool as opool
+from gpu_util import (DecodeRun, bits, check_close, oracle_decode_all_pairs, shared_decode_inputs,
+                      storage_bits, to_dev, to_f64)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -73,41 +75,45 @@ FORTY_CHECK = [1, 2, 127, 128, 129, 130, 256, 1024, 3072, 6143, 6144]
 
 @pytest.mark.slow
 def test_forty_page_full_size():
+    """Every (sequence, head) at the listed steps and 5 seeded random ones, against
+    the oracle on all host cores; window-slot images bit for bit."""
     w = wl.FORTY_PAGE
     rng = np.random.default_rng(3)
     extra = sorted(set(rng.integers(3, w.steps, size=5).tolist()) - set(FORTY_CHECK))
     checks = sorted(set(FORTY_CHECK) | set(extra))
-    banner(f"40-page bf16 decode, full size, {w.steps} steps; checked {checks}")
-    run = DecodeRun(w)
-    got = run.run(w.steps, keep=checks, chunk=512)
-    all_bh = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    banner(f"40-page bf16 decode, full size, {w.steps} steps; every (b,h) at {checks}")
+    with opool.SharedArrays() as arrays:
+        kref, vref, steps = shared_decode_inputs(w, arrays, w.steps)
+        run = DecodeRun(w, ref=(kref, vref))
+        got = run.run(w.steps, keep=checks, chunk=512, steps=steps)
+        run.check_cache_image(bs=[0, 17, 31], heads=[0, 7, 15], ref_rows=[0, 1, 5000, 10271])
+        assert rs.rswa_check_device_error(run.cache.desc) == 0
+        del run
+        print(f"oracle: {len(checks)} steps x {w.batch * w.heads} (b,h) on {opool.workers()} processes",
+              flush=True)
+        ref = oracle_decode_all_pairs(w, w.window, arrays, checks)
     for T in checks:
-        if T in (1, 128, 129, 6144):
-            bh = all_bh
-        else:
-            idx = rng.choice(len(all_bh), size=48, replace=False)
-            bh = [all_bh[i] for i in idx]
-        ref = run.oracle(T, bh)
-        g = np.asarray([got[T][b, h] for b, h in bh])
-        ma, rel = check_close(g, ref, "bf16", f"40-page T={T}")
-        print(f"T={T}: {len(bh)} (b,h) max|d|={ma:.3e} rel={rel:.3e}", flush=True)
-    run.check_cache_image(bs=[0, 17, 31], heads=[0, 7, 15], ref_rows=[0, 1, 5000, 10271])
-    assert rs.rswa_check_device_error(run.cache.desc) == 0
+        ma, rel = check_close(got[T], ref[T], "bf16", f"40-page T={T}")
+        print(f"T={T}: all {w.batch * w.heads} (b,h) max|d|={ma:.3e} worst (b,h) rel={rel:.3e}", flush=True)
 
 
 @pytest.mark.slow
 def test_forty_page_full_attention_contrast():
-    """Same kernels with the window >= all outputs: the cache grows as L_m + T (Eq. 5)."""
+    """Same kernels with the window >= all outputs: the cache grows as L_m + T (Eq. 5).
+    Every (sequence, head) at each checked step."""
     w = wl.FORTY_PAGE
     checks = [1, 129, 2048, 6144]
-    banner("40-page full-attention contrast (window = 6144)")
-    run = DecodeRun(w, window=w.steps)
-    got = run.run(w.steps, keep=checks, chunk=512)
-    bh = [(0, 0), (5, 3), (31, 15), (12, 8)]
+    banner("40-page full-attention contrast (window = 6144), every (b,h)")
+    with opool.SharedArrays() as arrays:
+        kref, vref, steps = shared_decode_inputs(w, arrays, w.steps)
+        run = DecodeRun(w, window=w.steps, ref=(kref, vref))
+        got = run.run(w.steps, keep=checks, chunk=512, steps=steps)
+        assert rs.rswa_check_device_error(run.cache.desc) == 0
+        del run
+        ref = oracle_decode_all_pairs(w, w.steps, arrays, checks)
     for T in checks:
-        ref = run.oracle(T, bh)
-        ma, rel = check_close(np.asarray([got[T][b, h] for b, h in bh]), ref, "bf16", f"contrast T={T}")
-        print(f"contrast T={T}: max|d|={ma:.3e} rel={rel:.3e}", flush=True)
+        ma, rel = check_close(got[T], ref[T], "bf16", f"contrast T={T}")
+        print(f"contrast T={T}: max|d|={ma:.3e} worst (b,h) rel={rel:.3e}", flush=True)
 
 
 def test_ragged_batch_one_fused_step():
@@ -453,6 +459,8 @@ def test_masked_rows_agree_with_decode_kernel():
 @pytest.mark.slow
 @pytest.mark.parametrize("mode", [rs.RSWA_PREFIX_CAUSAL, rs.RSWA_PREFIX_FULL])
 def test_packed_32k_sampled_rows(mode):
+    """All heads of: the rows at the segment and window edges, both edge rows of
+    every 128-row tile, and 2048 seeded random rows (oracle on all host cores)."""
     mw = wl.PACKED_32K
     N, L_m, n, H = mw.seq_len, mw.ref_len, mw.window, mw.heads
     banner(f"packed 32K masked forward, N={N} L_m={L_m} n={n} H={H} mode={mode}")
@@ -462,26 +470,22 @@ def test_packed_32k_sampled_rows(mode):
     rs.rswa_masked_attn(Qd, Kd, Vd, out, N, L_m, n, H, 128, rs.RSWA_BF16, mode, 0.0)
     torch.cuda.synchronize()
     got = to_f64(out)
+    del Qd, Kd, Vd, out
     rng = np.random.default_rng(11)
     special = [0, 1, L_m - 2, L_m - 1, L_m, L_m + 1, L_m + n - 2, L_m + n - 1, L_m + n, L_m + n + 1,
                4095, 4096, 4223, 4224, N - 1]
-    edges = [e for t in rng.choice(N // 128, 24, replace=False) for e in (128 * t, 128 * t + 127)]
-    rows = sorted(set(special + edges + rng.integers(0, N, 48).tolist()))
-    K64 = wl.to_f64(K, "bf16")
-    V64 = wl.to_f64(V, "bf16")
-    Q64 = wl.to_f64(Q[rows], "bf16")
-    ref = orc.masked_attention_rows(_RowView(Q64, rows), K64, V64, rows, L_m, n, mw.scale, mode)
-    ma, rel = check_close(got[rows], ref, "bf16", f"packed 32K sampled rows, mode {mode}")
-    print(f"packed 32K: {len(rows)} rows x {H} heads max|d|={ma:.3e} rel={rel:.3e}")
-
-
-class _RowView:
-    """Indexes like the full Q array for the sampled rows only."""
-
-    def __init__(self, q_rows, rows):
-        self.q = q_rows
-        self.pos = {r: i for i, r in enumerate(rows)}
-        self.shape = (max(rows) + 1,) + q_rows.shape[1:]
-
-    def __getitem__(self, i):
-        return self.q[self.pos[int(i)]]
+    edges = [e for t in range(N // 128) for e in (128 * t, 128 * t + 127)]
+    rows = sorted(set(special + edges + rng.choice(N, 2048, replace=False).tolist()))
+    print(f"oracle: {len(rows)} rows x {H} heads on {opool.workers()} processes", flush=True)
+    with opool.SharedArrays() as arrays:
+        for name, a in (("Q", Q), ("K", K), ("V", V)):
+            arrays.put(name, wl.bf16_bits_to_f32(a))   # exact values of the bf16 inputs
+        chunks = [rows[i::64] for i in range(64)]
+        parts = opool.pool_map(opool.masked_rows_job,
+                               [(c, L_m, n, mw.scale, mode) for c in chunks], arrays)
+    ref = np.empty((len(rows), H, 128))
+    pos = {r: i for i, r in enumerate(rows)}
+    for c, part in zip(chunks, parts):
+        ref[[pos[r] for r in c]] = part
+    ma, rel = check_close(got[rows], ref, "bf16", f"packed 32K rows, mode {mode}")
+    print(f"packed 32K: {len(rows)} rows x {H} heads max|d|={ma:.3e} worst (row, head) rel={rel:.3e}")

@@ -15,7 +15,7 @@ import torch
 import oracle.rswa as orc
 import reference_sliding_window_amd as rs
 import workloads as wl
-from gpu_util import bits, to_dev, to_f64
+from gpu_util import bits, check_grad, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -30,19 +30,6 @@ def banner(msg):
 
 def dev_i32(a):
     return torch.tensor(np.asarray(a, np.int32), dtype=torch.int32, device="cuda")
-
-
-def check_grad(got, ref, what):
-    d = got - ref
-    scale = max(1.0, float(np.abs(ref).max()) if ref.size else 1.0)
-    maxabs = float(np.abs(d).max()) if d.size else 0.0
-    rel = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300))
-    assert np.isfinite(got).all(), f"{what}: non-finite output"
-    if np.linalg.norm(ref) == 0.0:
-        rel = 0.0
-    assert maxabs <= 2e-2 * scale and rel <= 1e-2, \
-        f"{what}: max|d|={maxabs:.3e} (<= {2e-2 * scale:.3e}) rel={rel:.3e} (<= 1e-2)"
-    return maxabs, rel
 
 
 class PackRun:
