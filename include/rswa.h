@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define RSWA_ABI_VERSION 6
+#define RSWA_ABI_VERSION 7
 
 #if defined(__GNUC__)
 #define RSWA_API __attribute__((visibility("default")))
@@ -146,6 +146,19 @@ RSWA_API rswa_status_t rswa_append_kv(const rswa_cache_t *cache, const void *k_n
                              const uint8_t *active, void *stream);
 
 /*
+ * Workspace bytes needed by rswa_decode_attn with the library's split choice
+ * (num_splits = 0) for a cache of `batch` sequences of `num_heads` heads of
+ * dimension head_dim whose longest sequence holds max_len = max_ref_len +
+ * window slots: the per-split partial softmax states of the fixed-capacity
+ * cache (yhxrc page, "R-SWA 如何穩住長程解碼？"; 夜雨聆风 page, "为什么它能”无限”读下去？
+ * 关键在 KV cache 恒定"). Equals rswa_decode_workspace_size(cache, 0) for a
+ * descriptor with those sizes. Returns 0 for invalid sizes (batch or num_heads
+ * < 1, head_dim not 64 or 128, max_len < 1).
+ */
+RSWA_API size_t rswa_workspace_size(int32_t batch, int32_t num_heads, int32_t head_dim,
+                                    int32_t max_len);
+
+/*
  * Workspace bytes needed by rswa_decode_attn for this cache descriptor and
  * split count (0 = the library's choice). Returns 0 for an invalid
  * descriptor. The workspace holds per-split partial softmax states.
@@ -199,6 +212,11 @@ RSWA_API rswa_status_t rswa_decode_attn(const rswa_cache_t *cache, const void *q
  * lse: NULL, or device float [num_heads][seq_len] receiving each row's natural
  * log of the softmax normaliser, log sum_j exp(scale q_i.k_j) over the visible
  * keys (the input the backward pass needs).
+ * scale: 0 selects 1/sqrt(head_dim); otherwise finite and > 0. The packed
+ * kernels track each row's maximum of the unscaled scores and mask with -inf
+ * before scaling, which needs a positive scale; a negative one is rejected
+ * with RSWA_ERR_SHAPE here and in every other packed call (varlen, prefill and
+ * both backward calls). The decode calls accept any finite scale.
  */
 RSWA_API rswa_status_t rswa_masked_attn(const void *q, const void *k, const void *v, void *out,
                                float *lse, int32_t seq_len, int32_t ref_len, int32_t window,

@@ -42,7 +42,7 @@ RSWA_DEVERR_ALIGN = 8
 RSWA_DEVERR_PACK = 16
 
 EXPORTED = ("rswa_abi_version", "rswa_status_str", "rswa_cache_init", "rswa_append_kv",
-            "rswa_decode_workspace_size", "rswa_decode_attn", "rswa_masked_attn",
+            "rswa_workspace_size", "rswa_decode_workspace_size", "rswa_decode_attn", "rswa_masked_attn",
             "rswa_masked_attn_varlen", "rswa_prefill", "rswa_masked_bwd_workspace_size",
             "rswa_masked_attn_bwd", "rswa_masked_bwd_varlen_workspace_size",
             "rswa_masked_attn_bwd_varlen", "rswa_decode_graph_create", "rswa_decode_graph_launch",
@@ -90,6 +90,7 @@ def _lib() -> ctypes.CDLL:
             "rswa_status_str": (ctypes.c_char_p, [I32]),
             "rswa_cache_init": (I32, [D, P, P, P, P]),
             "rswa_append_kv": (I32, [D, P, P, P, P]),
+            "rswa_workspace_size": (SZ, [I32, I32, I32, I32]),
             "rswa_decode_workspace_size": (SZ, [D, I32]),
             "rswa_decode_attn": (I32, [D, P, P, P, P, F, I32, P, SZ, P]),
             "rswa_masked_attn": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, P]),
@@ -165,6 +166,10 @@ def rswa_append_kv(desc: CacheDesc, k_new, v_new, active=None, stream=None, chec
     st = _lib().rswa_append_kv(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(active),
                                _stream(stream))
     return _check(st, "rswa_append_kv") if check else st
+
+
+def rswa_workspace_size(batch: int, num_heads: int, head_dim: int, max_len: int) -> int:
+    return _lib().rswa_workspace_size(batch, num_heads, head_dim, max_len)
 
 
 def rswa_decode_workspace_size(desc: CacheDesc, num_splits: int = 0) -> int:

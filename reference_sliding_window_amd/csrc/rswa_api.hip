@@ -187,6 +187,13 @@ rswa_status_t rswa_append_kv(const rswa_cache_t *cache, const void *k_new, const
   return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
 }
 
+size_t rswa_workspace_size(int32_t batch, int32_t num_heads, int32_t head_dim, int32_t max_len) {
+  if (batch < 1 || num_heads < 1 || (head_dim != 64 && head_dim != 128) || max_len < 1) return 0;
+  if ((int64_t)batch * num_heads > INT32_MAX / 2) return 0;
+  const SplitPlan plan = plan_decode_splits(batch, num_heads, max_len, 0);
+  return decode_workspace_layout(batch, num_heads, head_dim, plan.splits).total;
+}
+
 size_t rswa_decode_workspace_size(const rswa_cache_t *cache, int32_t num_splits) {
   if (check_cache(cache) != RSWA_OK || num_splits < 0) return 0;
   const SplitPlan plan = plan_decode_splits(cache->batch, cache->num_heads,
@@ -263,7 +270,7 @@ rswa_status_t rswa_masked_attn(const void *q, const void *k, const void *v, void
   if ((int64_t)seq_len * num_heads * head_dim >= ((int64_t)1 << 31)) return RSWA_ERR_CAPACITY;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RSWA_ERR_ALIGN;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RSWA_ERR_ALIGN;
-  if (!isfinite(scale)) return RSWA_ERR_SHAPE;
+  if (!isfinite(scale) || scale < 0.f) return RSWA_ERR_SHAPE;  // see rswa_masked_attn
   if (seq_len == 0) return RSWA_OK;
   MaskedParams p{};
   p.q = q;
@@ -305,7 +312,7 @@ rswa_status_t rswa_masked_attn_varlen(const void *q, const void *k, const void *
   if (((reinterpret_cast<uintptr_t>(cu_seqlens) | reinterpret_cast<uintptr_t>(ref_lens)) & 3u) != 0)
     return RSWA_ERR_ALIGN;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RSWA_ERR_ALIGN;
-  if (!isfinite(scale)) return RSWA_ERR_SHAPE;
+  if (!isfinite(scale) || scale < 0.f) return RSWA_ERR_SHAPE;  // see rswa_masked_attn
   if (num_seqs == 0 || total_tokens == 0 || max_seq_len == 0) return RSWA_OK;
   MaskedParams p{};
   p.q = q;
@@ -343,7 +350,7 @@ rswa_status_t rswa_prefill(const rswa_cache_t *cache, const void *q, const void 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RSWA_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return RSWA_ERR_ALIGN;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RSWA_ERR_ALIGN;
-  if (!isfinite(scale)) return RSWA_ERR_SHAPE;
+  if (!isfinite(scale) || scale < 0.f) return RSWA_ERR_SHAPE;  // see rswa_masked_attn
   const int64_t qblocks = max_seq_len > 0 ? (max_seq_len + 127) / 128 : 1;
   if ((int64_t)cache->batch * cache->num_heads * qblocks >= ((int64_t)1 << 31)) return RSWA_ERR_CAPACITY;
   // One launch: the packed forward with the hand-off fused in (every sequence
@@ -403,7 +410,7 @@ rswa_status_t rswa_masked_attn_bwd(const void *q, const void *k, const void *v, 
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return RSWA_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RSWA_ERR_ALIGN;
-  if (!isfinite(scale)) return RSWA_ERR_SHAPE;
+  if (!isfinite(scale) || scale < 0.f) return RSWA_ERR_SHAPE;  // see rswa_masked_attn
   if (num_parts < 0 || num_parts > kMaxBwdParts) return RSWA_ERR_SHAPE;
   if (seq_len == 0) return RSWA_OK;
   const BwdPlan plan = plan_masked_bwd(seq_len, ref_len, num_heads, num_parts);
@@ -476,7 +483,7 @@ rswa_status_t rswa_masked_attn_bwd_varlen(const void *q, const void *k, const vo
   if (((reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(cu_seqlens) |
         reinterpret_cast<uintptr_t>(ref_lens)) & 3u) != 0)
     return RSWA_ERR_ALIGN;
-  if (!isfinite(scale)) return RSWA_ERR_SHAPE;
+  if (!isfinite(scale) || scale < 0.f) return RSWA_ERR_SHAPE;  // see rswa_masked_attn
   if (num_seqs == 0 || total_tokens == 0 || max_seq_len == 0) return RSWA_OK;
   const size_t need = rswa_masked_bwd_varlen_workspace_size(total_tokens, num_heads);
   if (workspace == nullptr) return RSWA_ERR_NULL;

@@ -315,3 +315,33 @@ def test_check_device_error_null_arguments():
     assert lib.rswa_check_device_error(None, ctypes.byref(flags), None) == rs.RSWA_ERR_NULL
     desc = good_desc()
     assert lib.rswa_check_device_error(ctypes.byref(desc), None, None) == rs.RSWA_ERR_NULL
+
+
+def test_workspace_size_by_sizes_matches_descriptor_form():
+    """rswa_workspace_size(batch, heads, head_dim, max_len) is the library's split
+    choice for a cache whose longest sequence holds max_len = max_ref_len + window slots."""
+    for B, H, d, L, n in ((32, 16, 128, 10272, 128), (1, 16, 128, 288, 128), (64, 16, 128, 12832, 128),
+                          (2, 16, 128, 10272, 128), (1, 2, 64, 64, 8), (3, 4, 64, 0, 5)):
+        desc = good_desc(batch=B, num_heads=H, head_dim=d, max_ref_len=L, window=n)
+        assert rs.rswa_workspace_size(B, H, d, L + n) == rs.rswa_decode_workspace_size(desc, 0) > 0
+    ws = rs.rswa_workspace_size
+    assert ws(0, 16, 128, 100) == 0
+    assert ws(1, 0, 128, 100) == 0
+    assert ws(1, 16, 96, 100) == 0
+    assert ws(1, 16, 128, 0) == 0
+    assert ws(2 ** 30, 16, 128, 100) == 0
+
+
+def test_packed_calls_reject_a_negative_scale():
+    """The packed kernels need scale > 0 (or 0 for the default); decode accepts any finite scale."""
+    neg = -0.125
+    assert rs.rswa_masked_attn(A, A, A, A, 300, 40, 8, 2, 128, scale=neg, check=False) == rs.RSWA_ERR_SHAPE
+    assert rs.rswa_masked_attn_varlen(A, A, A, A, A, A + 64, 3, 900, 400, 8, 2, 128, scale=neg,
+                                      check=False) == rs.RSWA_ERR_SHAPE
+    assert rs.rswa_prefill(good_desc(), A, A, A, A, A, 500, 300, scale=neg, check=False) == rs.RSWA_ERR_SHAPE
+    ws = rs.rswa_masked_bwd_workspace_size(300, 40, 2)
+    assert rs.rswa_masked_attn_bwd(A, A, A, A, A, A, A, A, A, 300, 40, 8, 2, 128, scale=neg, workspace=A,
+                                   workspace_bytes=ws, check=False) == rs.RSWA_ERR_SHAPE
+    wsv = rs.rswa_masked_bwd_varlen_workspace_size(300, 2)
+    assert rs.rswa_masked_attn_bwd_varlen(A, A, A, A, A, A, A, A, A, A, A, 2, 300, 200, 8, 2, 128, scale=neg,
+                                          workspace=A, workspace_bytes=wsv, check=False) == rs.RSWA_ERR_SHAPE
