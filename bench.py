@@ -3,15 +3,18 @@
 
 A step is one fused append + attend decode step of the 40-page workload
 (B = 32 sequences, H = 16 heads, d = 128, L_m = 10272, n = 128, bf16, one
-attention layer): one call of rswa_decode_attn. W warm-up steps run first
-(they also fill the 128-slot window), then exactly K steps are timed with HIP
-events on the launch stream. All inputs (reference K/V, per-step q/k/v) are
-resident in HBM before the timed region.
+attention layer): one call of rswa_decode_attn. The first n = 128 steps fill
+the window (untimed), W warm-up steps follow, then exactly K steps are timed
+back to back with HIP events on the launch stream, so every timed step sees the
+full L_m + n slots; K further steps are timed one by one for the median and
+p10/p90. All inputs (reference K/V, per-step q/k/v) are resident in HBM before
+the timed region.
 
 Printed: one JSON line. `value` is decode tokens/s (B / step time). The
 `roofline` object prices the decode kernel's algorithmic bytes (every visible
 K/V row once, plus q, out and the new k/v) against the 8 TB/s HBM peak.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same step.
+`cpu_baseline` times the CPU oracle on the whole last timed step, on the
+host's cores.
 Secondary lines of the same JSON: the full-attention contrast (cache L_m + T)
 at a few decode lengths, and the packed 32K masked forward (both prefix modes)
 and its backward, a multi-document 32K pack, the prefill -> decode hand-off
@@ -90,39 +93,31 @@ def event_time_ms(fn, iters, stream):
     return a.elapsed_time(b)
 
 
-def cpu_baseline(w, kref, vref, T, budget_s):
-    """Time the oracle on (sequence, head) pairs of decode step T until budget_s elapses."""
-    import oracle.rswa as orc
+def cpu_baseline(w, kref, vref, T):
+    """Time the oracle on every (sequence, head) of decode step T (all B x H pairs, the
+    whole step) on the host's cores: one worker process per core, BLAS on one thread
+    each, inputs in shared memory before the clock starts."""
+    import oracle.pool as opool
     import workloads as wl
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    first = max(1, T - w.window + 1)
-    q, k, v = wl.steps_qkv(w, first, T)
-    pairs = [(b, h) for b in range(w.batch) for h in range(w.heads)]
-    rng = np.random.default_rng(0)
-    order = rng.permutation(len(pairs))
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx:
-        ctx.__enter__()
-    try:
-        done, t0 = 0, time.perf_counter()
-        while done < len(order) and time.perf_counter() - t0 < budget_s:
-            b, h = pairs[order[done]]
-            orc.decode_output(wl.to_f64(q[-1, b, h], w.dtype), wl.to_f64(kref[b, h], w.dtype),
-                              wl.to_f64(vref[b, h], w.dtype), wl.to_f64(k[:, b, h], w.dtype),
-                              wl.to_f64(v[:, b, h], w.dtype), first, w.ref_len, w.window, T, w.scale)
-            done += 1
-        el = time.perf_counter() - t0
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
-    step_s = el / done * len(pairs)
-    return {"value": w.batch / step_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"40-page decode step T={T}: {done} of {len(pairs)} (sequence, head) pairs "
-                      f"in {el:.1f} s on 1 thread (BLAS limited to 1), scaled to all {len(pairs)}; "
-                      f"host has {len(os.sched_getaffinity(0))} cores available"}
+    with opool.SharedArrays() as arrays:
+        arrays.put("kref", kref)
+        arrays.put("vref", vref)
+        first = max(1, T - w.window + 1)
+        for name, a in zip(("q", "k", "v"), wl.steps_qkv(w, first, T)):
+            arrays.new(name, (T,) + a.shape[1:], a.dtype)[first - 1:T] = a   # the job reads only these
+        tasks = [(w.dtype, w.ref_len, w.window, w.scale, b, list(range(w.heads)), [T])
+                 for b in range(w.batch)]
+        with opool.OraclePool(arrays) as pool:
+            pool.map(opool.ready, range(4 * pool.processes))   # every worker up before timing
+            t0 = time.perf_counter()
+            pool.map(opool.decode_sequence_job, tasks)
+            el = time.perf_counter() - t0
+            cores = pool.processes
+    return {"value": w.batch / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the whole 40-page decode step T={T} (steady state, window full): all "
+                      f"{w.batch * w.heads} (sequence, head) pairs in {el:.1f} s wall on {cores} worker "
+                      f"processes (one per host core, BLAS on one thread each; {cores * el:.0f} core-seconds); "
+                      f"host reports {len(os.sched_getaffinity(0))} cores available"}
 
 
 def device_facts(torch):
@@ -157,47 +152,29 @@ def gemm_tflops(torch, stream, m=8192):
     return 2 * m ** 3 / (ms * 1e-3) / 1e12
 
 
-class _OneRow:
-    """Indexes like the full Q array for one row (the oracle reads only that row)."""
-
-    def __init__(self, row, i, shape):
-        self.row, self.i, self.shape = row, i, shape
-
-    def __getitem__(self, i):
-        assert int(i) == self.i
-        return self.row
-
-
-def cpu_masked_rows(mw, Q, K, V, budget_s):
-    """Time the oracle's packed forward on a few output rows (all heads) and scale to all rows."""
-    import oracle.rswa as orc
+def cpu_masked_rows(mw, Q, K, V, rows_per_core=48):
+    """Time the oracle's packed forward on random output rows (all heads) on the host's
+    cores and scale to all rows."""
+    import oracle.pool as opool
     import workloads as wl
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    K64, V64 = wl.to_f64(K, "bf16"), wl.to_f64(V, "bf16")
-    rng = np.random.default_rng(1)
-    rows = rng.integers(mw.ref_len, mw.seq_len, 64)
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx:
-        ctx.__enter__()
-    try:
-        done, t0 = 0, time.perf_counter()
-        while done < len(rows) and time.perf_counter() - t0 < budget_s:
-            i = int(rows[done])
-            orc.masked_attention_rows(_OneRow(wl.to_f64(Q[i], "bf16"), i, Q.shape), K64, V64, [i], mw.ref_len,
-                                      mw.window, mw.scale)
-            done += 1
-        el = time.perf_counter() - t0
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
-    per_row = el / done
+    with opool.SharedArrays() as arrays:
+        for name, a in (("Q", Q), ("K", K), ("V", V)):
+            arrays.put(name, wl.bf16_bits_to_f32(a))   # exact values of the bf16 inputs
+        with opool.OraclePool(arrays) as pool:
+            cores = pool.processes
+            rng = np.random.default_rng(1)
+            rows = rng.integers(mw.ref_len, mw.seq_len, rows_per_core * cores).tolist()
+            tasks = [(rows[i::cores], mw.ref_len, mw.window, mw.scale, 0) for i in range(cores)]
+            pool.map(opool.ready, range(4 * cores))
+            t0 = time.perf_counter()
+            pool.map(opool.masked_rows_job, tasks)
+            el = time.perf_counter() - t0
+    per_row = el / len(rows)
     return {"seconds_per_output_row_all_heads": per_row,
-            "extrapolated_seconds_for_all_rows": per_row * mw.seq_len, "cores": 1, "kind": "oracle",
-            "sample": f"{done} random output rows x {mw.heads} heads in {el:.1f} s on 1 thread; output rows "
-                      f"see the most keys, so the extrapolation to all {mw.seq_len} rows is an upper bound"}
+            "extrapolated_seconds_for_all_rows": per_row * mw.seq_len, "cores": cores, "kind": "oracle",
+            "sample": f"{len(rows)} random output rows x {mw.heads} heads in {el:.1f} s wall on {cores} worker "
+                      f"processes (BLAS on one thread each); output rows see the most keys, so the "
+                      f"extrapolation to all {mw.seq_len} rows is an upper bound"}
 
 
 def per_step_curve(torch, rs, w, stream, Tmax):
@@ -247,7 +224,6 @@ def main():
     ap.add_argument("--steps", type=int, default=2048)
     ap.add_argument("--warmup", type=int, default=256)
     ap.add_argument("--splits", type=int, default=0, help="decode key splits per (seq, head); 0 = library")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the contrast and masked lines")
     ap.add_argument("--layers", type=int, default=12,
@@ -296,7 +272,11 @@ def main():
     rs.rswa_cache_init(cache.desc, kd, vd, ref_base)
     torch.cuda.synchronize()
     del kd, vd
-    steps_total = W + K
+    # outputs 1..n fill the window (untimed), then W warm-up and K timed steps, then K
+    # more steps timed one by one for the per-step distribution: every timed step has
+    # the full L_m + n slots visible (the steady state of Eq. (6))
+    fill = n
+    steps_total = fill + W + 2 * K
     qs = torch.empty((steps_total, B, H, d), dtype=torch.bfloat16, device="cuda")
     ks = torch.empty_like(qs)
     vs = torch.empty_like(qs)
@@ -313,16 +293,28 @@ def main():
     def step(i):
         rs.rswa_decode_attn(cache.desc, qs[i], out, ks[i], vs[i], 0.0, args.splits, ws, stream=stream)
 
-    for i in range(W):
+    for i in range(fill + W):
         step(i)
     torch.cuda.synchronize()
-    ms = event_time_ms(lambda i: step(W + i), K, stream)
+    t_first = fill + W + 1                       # output index T of the first timed step
+    ms = event_time_ms(lambda i: step(fill + W + i), K, stream)
     ms_per_step = ms / K
+    # the same number of further steps, each between its own pair of events
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(fill + W + K + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) for a, b in ev])
     flags = rs.rswa_check_device_error(cache.desc)
     if flags:
         print(f"device error flags {flags}", file=sys.stderr)
         sys.exit(1)
-    alg_bytes = sum(decode_bytes(B, H, d, L, n, T) for T in range(W + 1, W + K + 1)) / K
+    if int(cache.step[0].item()) != steps_total:
+        print("decode step counter did not advance as expected", file=sys.stderr)
+        sys.exit(1)
+    alg_bytes = sum(decode_bytes(B, H, d, L, n, T) for T in range(t_first, t_first + K)) / K
     achieved = alg_bytes / (ms_per_step * 1e-3) / 1e9
     traffic = read_traffic(1)
     achievable = probe_read_GBps(torch, rs, stream)
@@ -340,14 +332,21 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "head_dim": d, "ref_len": L,
-                   "window": n, "layers": 1, "timed_decode_steps": f"T={W + 1}..{W + K}",
+                   "window": n, "layers": 1, "timed_decode_steps": f"T={t_first}..{t_first + K - 1}",
+                   "window_fill_steps": f"T=1..{fill} untimed, then warm-up T={fill + 1}..{fill + W}",
                    "splits": args.splits or "library"},
         "hbm_GBps": achieved,
         "hbm_frac_of_peak": achieved / HBM_PEAK_GBS,
+        "per_step_ms": {"median": float(np.median(per_step)), "p10": float(np.percentile(per_step, 10)),
+                        "p90": float(np.percentile(per_step, 90)), "mean": float(per_step.mean()),
+                        "steps": f"T={t_first + K}..{t_first + 2 * K - 1}",
+                        "note": "each step between its own pair of HIP events (the event records add "
+                                "a little to every step; ms_per_step times the K steps back to back)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "rswa decode step (split-K attention, merged in the same launch when the plan has one chunk per (sequence, head)), one call",
                      "algorithmic_bytes_per_launch": alg_bytes,
+                     "traffic_steps": "steady state (all L_m + n slots visible), as the timed steps",
                      "achievable_read_GBps": achievable, "frac_of_achievable": achieved / achievable},
         "device": device_facts(torch),
     }
@@ -391,24 +390,25 @@ def main():
                       for _ in range(3))
         rout = torch.empty_like(rq)
         rws = rc.workspace()
-
-        def ragged_step(i):
-            rc.step.copy_(saved)   # back to the state before output t_now (idempotent rewrite)
-            rs.rswa_decode_attn(rc.desc, rq, rout, rk, rv, 0.0, 0, rws, stream=stream)
-
+        rc.step.copy_(saved)   # every sequence just before its output t_now
+        r_steps = 50
+        ragged_step = lambda i: rs.rswa_decode_attn(rc.desc, rq, rout, rk, rv, 0.0, 0, rws, stream=stream)
         for _ in range(3):
             ragged_step(0)
-        ms_rg = event_time_ms(ragged_step, 50, stream) / 50
+        ms_rg = event_time_ms(ragged_step, r_steps, stream) / r_steps
         if rs.rswa_check_device_error(rc.desc):
             print("ragged step reported device errors", file=sys.stderr)
             sys.exit(1)
-        rbytes = sum(rw.heads * (Lb + min(rw.window, t)) * rw.head_dim * 2 * 2 for Lb, t in zip(rrefs, rtnow)) \
+        # the timed steps append outputs t_now + 3 .. t_now + 52 of every sequence
+        rbytes = sum(rw.heads * (Lb + min(rw.window, t + 3 + i)) * rw.head_dim * 2 * 2
+                     for i in range(r_steps) for Lb, t in zip(rrefs, rtnow)) / r_steps \
             + 4 * rw.batch * rw.heads * rw.head_dim * 2
         result["ragged_64"] = {
             "workload": rw.name, "batch": rw.batch, "ms_per_step": ms_rg, "tokens_per_s": rw.batch / (ms_rg * 1e-3),
             "algorithmic_bytes": rbytes, "GBps": rbytes / (ms_rg * 1e-3) / 1e9,
             "frac_of_peak": rbytes / (ms_rg * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "note": "includes a 256-byte step-counter restore before each step"}
+            "note": f"{r_steps} consecutive fused steps after 3 warm-up steps, each sequence from its own "
+                    "decode position (pages ~ U{1..50}, T ~ U{1..8192}); no state restored in between"}
         del rc, rq, rk, rv, rout, rws
 
         gemm = gemm_tflops(torch, stream)
@@ -457,7 +457,7 @@ def main():
                                 "window": mw.window, "heads": mw.heads,
                                 "measured_bf16_gemm_TFLOPs": gemm, "gemm": "8192^3 bf16 torch.matmul", **masked}
         if not args.no_cpu_baseline:
-            result["cpu_baseline_masked"] = cpu_masked_rows(mw, Q, Kp, Vp, min(10.0, args.cpu_seconds))
+            result["cpu_baseline_masked"] = cpu_masked_rows(mw, Q, Kp, Vp)
 
         # several documents per 32K pack (samples independent), forward on matrix cores
         cu, refs = wl.varlen_pack_layout(mw.seq_len, mw.base_seed)
@@ -664,7 +664,7 @@ def main():
     if args.curve:
         result["per_step_curve"] = per_step_curve(torch, rs, w, stream, w.steps)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, kref, vref, W + K, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, kref, vref, t_first + K - 1)
     result["setup_s"] = setup_s
     print(json.dumps(result), flush=True)
 
