@@ -17,6 +17,8 @@ from __future__ import annotations
 
 import multiprocessing as mp
 import os
+import time
+import weakref
 from multiprocessing import shared_memory
 
 import numpy as np
@@ -25,6 +27,7 @@ from . import rswa as orc
 
 _SHARED: dict = {}
 _SEGMENTS: list = []
+_RETIRED: list = []
 _LIMITS = None
 
 
@@ -48,9 +51,10 @@ class SharedArrays:
         dtype = np.dtype(dtype)
         nbytes = max(1, int(np.prod(shape)) * dtype.itemsize)
         seg = shared_memory.SharedMemory(create=True, size=nbytes)
-        self._segs[name] = seg
         self.specs[name] = (seg.name, tuple(int(s) for s in shape), dtype.str)
-        return np.ndarray(shape, dtype=dtype, buffer=seg.buf)
+        a = np.ndarray(shape, dtype=dtype, buffer=seg.buf)
+        self._segs[name] = (seg, weakref.ref(a))   # views of `a` keep it alive
+        return a
 
     def put(self, name: str, a: np.ndarray) -> np.ndarray:
         view = self.new(name, a.shape, a.dtype)
@@ -58,9 +62,19 @@ class SharedArrays:
         return view
 
     def release(self):
-        for seg in self._segs.values():
-            seg.close()
+        """Removes the segments' names and unmaps them; a segment the caller still
+        holds a view of stays mapped (until a later release finds it unused)."""
+        global _RETIRED
+        for seg, ref in self._segs.values():
             seg.unlink()
+            _RETIRED.append((seg, ref))
+        keep = []
+        for seg, ref in _RETIRED:
+            if ref() is None:
+                seg.close()
+            else:
+                keep.append((seg, ref))
+        _RETIRED = keep
         self._segs.clear()
         self.specs.clear()
 
@@ -98,8 +112,23 @@ class OraclePool:
         self._pool = mp.get_context("spawn").Pool(
             self.processes, initializer=_init, initargs=(arrays.specs if arrays else None,))
 
-    def map(self, fn, tasks):
-        return self._pool.map(fn, list(tasks), chunksize=1)
+    def map(self, fn, tasks, progress: str | None = None, task_timeout: float = 900.0):
+        """[fn(t) for t in tasks]. Raises TimeoutError if any result is more than
+        task_timeout seconds in coming (a worker that died, e.g. in its start-up,
+        is replaced by the pool and its task would otherwise never return). With
+        `progress`, prints a line (flushed) as every tenth of the tasks completes,
+        so a long oracle run shows it is alive."""
+        tasks = list(tasks)
+        out, t0, mark = [], time.perf_counter(), 1
+        it = self._pool.imap(fn, tasks, chunksize=1)
+        for _ in range(len(tasks)):
+            out.append(it.next(task_timeout))
+            if progress is not None and len(out) * 10 >= mark * len(tasks):
+                print(f"[oracle] {progress}: {len(out)}/{len(tasks)} tasks, "
+                      f"{time.perf_counter() - t0:.0f} s", flush=True)
+                while len(out) * 10 >= mark * len(tasks):
+                    mark += 1
+        return out
 
     def close(self):
         self._pool.close()
@@ -112,13 +141,14 @@ class OraclePool:
         self._pool.terminate() if exc[0] is not None else self.close()
 
 
-def pool_map(fn, tasks, arrays: SharedArrays | None = None, processes: int | None = None):
+def pool_map(fn, tasks, arrays: SharedArrays | None = None, processes: int | None = None,
+             progress: str | None = None):
     """[fn(t) for t in tasks] on a fresh OraclePool, order kept."""
     tasks = list(tasks)
     if not tasks:
         return []
     with OraclePool(arrays, min(processes or workers(), len(tasks))) as pool:
-        return pool.map(fn, tasks)
+        return pool.map(fn, tasks, progress)
 
 
 def ready(_=None):

@@ -482,7 +482,7 @@ def test_packed_32k_sampled_rows(mode):
             arrays.put(name, wl.bf16_bits_to_f32(a))   # exact values of the bf16 inputs
         chunks = [rows[i::64] for i in range(64)]
         parts = opool.pool_map(opool.masked_rows_job,
-                               [(c, L_m, n, mw.scale, mode) for c in chunks], arrays)
+                               [(c, L_m, n, mw.scale, mode) for c in chunks], arrays, progress="packed rows")
     ref = np.empty((len(rows), H, 128))
     pos = {r: i for i, r in enumerate(rows)}
     for c, part in zip(chunks, parts):
