@@ -201,6 +201,28 @@ RSWA_API rswa_status_t rswa_decode_attn(const rswa_cache_t *cache, const void *q
                                void *stream);
 
 /*
+ * rswa_decode_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops or harnesses that forbid hipMalloc): the
+ * same arguments, checks, kernels and results as rswa_decode_attn, but the
+ * per-split partial states live in a library-owned static device buffer of
+ * RSWA_NOALLOC_SCRATCH_BYTES (8 MiB) instead of a caller workspace. The call
+ * allocates nothing; each GPU the library runs on holds its own buffer until
+ * the process ends, and the first call on a device (that device current) looks
+ * up its address. Nothing in the buffer needs to start at zero (every call
+ * writes the partial states before it reads them).
+ *  Returns RSWA_ERR_WORKSPACE when rswa_decode_workspace_size(cache,
+ *  num_splits) exceeds RSWA_NOALLOC_SCRATCH_BYTES (e.g. 32 sequences x 16
+ *  heads with 64 splits), without enqueuing anything.
+ * All calls on one GPU share its buffer: calls that may overlap (different
+ * streams, or a graph replay beside an eager call) race on it and must be
+ * ordered by the caller.
+ */
+#define RSWA_NOALLOC_SCRATCH_BYTES (8u << 20)
+RSWA_API rswa_status_t rswa_decode_attn_noalloc(const rswa_cache_t *cache, const void *q, void *out,
+                                                const void *k_new, const void *v_new, float scale,
+                                                int32_t num_splits, void *stream);
+
+/*
  * Packed (teacher-forced) R-SWA forward over one sequence of seq_len tokens:
  * row i attends to key j iff j <= i and (j < ref_len or i - j < window); with
  * RSWA_PREFIX_FULL, rows i < ref_len instead attend to all j < ref_len. For a

@@ -42,7 +42,8 @@ RSWA_DEVERR_ALIGN = 8
 RSWA_DEVERR_PACK = 16
 
 EXPORTED = ("rswa_abi_version", "rswa_status_str", "rswa_cache_init", "rswa_append_kv",
-            "rswa_workspace_size", "rswa_decode_workspace_size", "rswa_decode_attn", "rswa_masked_attn",
+            "rswa_workspace_size", "rswa_decode_workspace_size", "rswa_decode_attn",
+            "rswa_decode_attn_noalloc", "rswa_masked_attn",
             "rswa_masked_attn_varlen", "rswa_prefill", "rswa_masked_bwd_workspace_size",
             "rswa_masked_attn_bwd", "rswa_masked_bwd_varlen_workspace_size",
             "rswa_masked_attn_bwd_varlen", "rswa_decode_graph_create", "rswa_decode_graph_launch",
@@ -93,6 +94,7 @@ def _lib() -> ctypes.CDLL:
             "rswa_workspace_size": (SZ, [I32, I32, I32, I32]),
             "rswa_decode_workspace_size": (SZ, [D, I32]),
             "rswa_decode_attn": (I32, [D, P, P, P, P, F, I32, P, SZ, P]),
+            "rswa_decode_attn_noalloc": (I32, [D, P, P, P, P, F, I32, P]),
             "rswa_masked_attn": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, P]),
             "rswa_masked_attn_varlen": (I32, [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
                                               I32, F, P]),
@@ -186,6 +188,13 @@ def rswa_decode_attn(desc: CacheDesc, q, out, k_new=None, v_new=None, scale: flo
                                  float(scale), int(num_splits), _ptr(workspace), int(workspace_bytes),
                                  _stream(stream))
     return _check(st, "rswa_decode_attn") if check else st
+
+
+def rswa_decode_attn_noalloc(desc: CacheDesc, q, out, k_new=None, v_new=None, scale: float = 0.0,
+                             num_splits: int = 0, stream=None, check=True) -> int:
+    st = _lib().rswa_decode_attn_noalloc(ctypes.byref(desc), _ptr(q), _ptr(out), _ptr(k_new), _ptr(v_new),
+                                         float(scale), int(num_splits), _stream(stream))
+    return _check(st, "rswa_decode_attn_noalloc") if check else st
 
 
 def rswa_masked_attn(q, k, v, out, seq_len: int, ref_len: int, window: int, num_heads: int,

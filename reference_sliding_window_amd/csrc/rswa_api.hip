@@ -8,6 +8,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "rswa_internal.h"
 
@@ -202,10 +203,15 @@ size_t rswa_decode_workspace_size(const rswa_cache_t *cache, int32_t num_splits)
       .total;
 }
 
-rswa_status_t rswa_decode_attn(const rswa_cache_t *cache, const void *q, void *out,
-                               const void *k_new, const void *v_new, float scale,
-                               int32_t num_splits, void *workspace, size_t workspace_bytes,
-                               void *stream) {
+}  // extern "C"
+
+namespace rswa {
+namespace {
+
+// Checks of a decode call that do not involve its workspace.
+rswa_status_t check_decode_args(const rswa_cache_t *cache, const void *q, const void *out,
+                                const void *k_new, const void *v_new, float scale,
+                                int32_t num_splits) {
   rswa_status_t st = check_cache(cache);
   if (st != RSWA_OK) return st;
   if (q == nullptr || out == nullptr) return RSWA_ERR_NULL;
@@ -214,6 +220,48 @@ rswa_status_t rswa_decode_attn(const rswa_cache_t *cache, const void *q, void *o
   if (k_new != nullptr && (!aligned16(k_new) || !aligned16(v_new))) return RSWA_ERR_ALIGN;
   if (!isfinite(scale)) return RSWA_ERR_SHAPE;
   if (num_splits < 0) return RSWA_ERR_SHAPE;
+  return RSWA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned decode workspace for callers that cannot allocate device
+// memory (rswa_decode_attn_noalloc). Each GPU holds its own copy of `scratch`
+// until the process ends; host code uses only the device address looked up
+// per device, never the array's name (a host-side stand-in).
+constexpr size_t kScratchBytes = (size_t)RSWA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up once per device, under a lock).
+rswa_status_t scratch_for_current_device(void **ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return RSWA_ERR_HIP;
+  if (dev >= kMaxDevices) return RSWA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return RSWA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return RSWA_OK;
+}
+
+}  // namespace
+}  // namespace rswa
+
+extern "C" {
+
+rswa_status_t rswa_decode_attn(const rswa_cache_t *cache, const void *q, void *out,
+                               const void *k_new, const void *v_new, float scale,
+                               int32_t num_splits, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  const rswa_status_t st = check_decode_args(cache, q, out, k_new, v_new, scale, num_splits);
+  if (st != RSWA_OK) return st;
   const SplitPlan plan = plan_decode_splits(cache->batch, cache->num_heads,
                                             cache->max_ref_len + cache->window, num_splits);
   const WorkspaceLayout ws = decode_workspace_layout(cache->batch, cache->num_heads,
@@ -254,6 +302,18 @@ rswa_status_t rswa_decode_attn(const rswa_cache_t *cache, const void *q, void *o
   const hipError_t e = launch_decode(p, cache->dtype, cache->head_dim,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
+}
+
+rswa_status_t rswa_decode_attn_noalloc(const rswa_cache_t *cache, const void *q, void *out,
+                                       const void *k_new, const void *v_new, float scale,
+                                       int32_t num_splits, void *stream) {
+  const rswa_status_t st = check_decode_args(cache, q, out, k_new, v_new, scale, num_splits);
+  if (st != RSWA_OK) return st;
+  if (rswa_decode_workspace_size(cache, num_splits) > kScratchBytes) return RSWA_ERR_WORKSPACE;
+  void *ws = nullptr;
+  const rswa_status_t sst = scratch_for_current_device(&ws);
+  if (sst != RSWA_OK) return sst;
+  return rswa_decode_attn(cache, q, out, k_new, v_new, scale, num_splits, ws, kScratchBytes, stream);
 }
 
 rswa_status_t rswa_masked_attn(const void *q, const void *k, const void *v, void *out,

@@ -345,3 +345,17 @@ def test_packed_calls_reject_a_negative_scale():
     wsv = rs.rswa_masked_bwd_varlen_workspace_size(300, 2)
     assert rs.rswa_masked_attn_bwd_varlen(A, A, A, A, A, A, A, A, A, A, A, 2, 300, 200, 8, 2, 128, scale=neg,
                                           workspace=A, workspace_bytes=wsv, check=False) == rs.RSWA_ERR_SHAPE
+
+
+def test_noalloc_decode_checks_before_touching_the_device():
+    """Argument checks and the buffer-size limit come first (nothing enqueued)."""
+    desc = good_desc(batch=32, num_heads=16, max_ref_len=10272, window=128)
+    call = lambda **kw: rs.rswa_decode_attn_noalloc(desc, **{**dict(q=A, out=A), **kw}, check=False)
+    assert rs.rswa_decode_workspace_size(desc, 64) > 8 << 20
+    assert call(num_splits=64) == rs.RSWA_ERR_WORKSPACE
+    assert call(q=None) == rs.RSWA_ERR_NULL
+    assert call(k_new=A) == rs.RSWA_ERR_NULL
+    assert call(out=A + 4) == rs.RSWA_ERR_ALIGN
+    assert call(scale=math.nan) == rs.RSWA_ERR_SHAPE
+    assert call(num_splits=-1) == rs.RSWA_ERR_SHAPE
+    assert rs.rswa_decode_attn_noalloc(good_desc(head_dim=96), A, A, check=False) == rs.RSWA_ERR_UNSUPPORTED
