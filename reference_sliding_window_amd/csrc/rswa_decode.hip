@@ -214,64 +214,59 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   if (threadIdx.x == 0) p.step[b] = T0 + 1;
 }
 
-// Split-K decode. Grid (H, B, splits), 4 waves. Workgroup (b, h, sp) owns the
-// key slots [sp*chunk, min(vis, (sp+1)*chunk)) of (b, h), vis = L_m + min(n, T).
-// Its waves take tiles of kRpl*U rows round-robin; lane group g (kLpr lanes)
-// of a wave follows rows g, g + kRpl, ... of each tile with its own online
-// softmax state, so the loop needs no cross-row communication.
+// Per-sequence facts every decode kernel derives the same way: the error bits
+// of sequence b and its visible slot count vis = L_m + min(n, T) (0 when flagged).
+struct SeqFacts {
+  int32_t L, T0, vis;
+  int64_t base;
+  int err;
+};
+
+template <int kEpl>
+__device__ __forceinline__ SeqFacts seq_facts(const DecodeParams &p, int b) {
+  SeqFacts f;
+  f.L = p.ref_len[b];
+  f.T0 = p.step[b];
+  f.base = p.seq_base[b];
+  const bool fused = p.k_new != nullptr;
+  f.err = seq_errors(f.L, p.max_ref_len, f.base, kEpl);
+  if (f.T0 < 0 || (fused && f.T0 == INT32_MAX)) f.err |= RSWA_DEVERR_STEP;
+  const int32_t T = fused ? f.T0 + 1 : f.T0;
+  f.vis = f.err ? 0 : f.L + min(p.window, T);
+  if (!f.err && f.vis == 0) f.err |= RSWA_DEVERR_EMPTY;
+  return f;
+}
+
+// Attention of one query (sequence b, head h) over the visible slots
+// [start, end) (start < end), by one workgroup of 4 waves: its waves take tiles
+// of kRpl*U rows round-robin; lane group g (kLpr lanes) of a wave follows rows
+// g, g + kRpl, ... of each tile with its own online softmax state, so the loop
+// needs no cross-row communication. The result is the chunk's partial state
+// (po[d], pml = {max, sum}) or, with write_out, the normalised output row.
 //
 // Fused append: the slot receiving the new token, star = L_m + (T0 mod n),
 // lies in exactly one chunk. That workgroup reads the new K/V from k_new/v_new
 // instead of the slot and also writes them into the slot; no other workgroup
 // reads the slot, so the evicted entry is never visible and there is no race.
 template <class E, int D, int U>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
+__device__ __forceinline__ void attend_range(const DecodeParams &p, int b, int h, const SeqFacts &f,
+                                             int start, int end, float *po, float *pml,
+                                             bool write_out) {
   using G = Geometry<E, D>;
   using S = typename E::storage;
   constexpr int kEpl = G::kEpl, kLpr = G::kLpr, kRpl = G::kRpl;
   constexpr int kTile = kRpl * U;
   constexpr int kWaves = 4;
-
-  const int b = blockIdx.y, h = blockIdx.x, sp = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane / kLpr, c = lane % kLpr;
   const int64_t bh = (int64_t)b * p.heads + h;
-  float *po = p.part_o + (bh * p.splits + sp) * D;
-  float *pml = p.part_ml + (bh * p.splits + sp) * 2;
-
-  const int32_t L = p.ref_len[b];
-  const int32_t T0 = p.step[b];
-  const int64_t base = p.seq_base[b];
   const bool fused = p.k_new != nullptr;
-  int err = seq_errors(L, p.max_ref_len, base, kEpl);
-  if (T0 < 0 || (fused && T0 == INT32_MAX)) err |= RSWA_DEVERR_STEP;
-  const int32_t T = fused ? T0 + 1 : T0;
-  const int32_t vis = err ? 0 : L + min(p.window, T);
-  if (!err && vis == 0) err |= RSWA_DEVERR_EMPTY;
-  if (sp == 0 && h == 0 && threadIdx.x == 0) {
-    p.seq_state[b] = (err || !fused) ? -1 : T0 + 1;
-    if (err) atomicOr(p.error, err);
-  }
+  const int32_t L = f.L;
 
-  const int start = sp * p.chunk;
-  const int end = min(vis, start + p.chunk);
-  if (err || start >= end) {  // empty partial state (one launch: a zero output)
-    if (p.one_launch) {
-      for (int i = threadIdx.x; i < D; i += 256) store_out<E>(p.out, bh * D + i, 0.f);
-      return;
-    }
-    for (int i = threadIdx.x; i < D; i += 256) po[i] = 0.f;
-    if (threadIdx.x == 0) {
-      pml[0] = kNegInf;
-      pml[1] = 0.f;
-    }
-    return;
-  }
-
-  const int64_t head_off = base + (int64_t)h * (L + p.window) * D;
+  const int64_t head_off = f.base + (int64_t)h * (L + p.window) * D;
   const S *kb = static_cast<const S *>(p.k) + head_off;
   const S *vb = static_cast<const S *>(p.v) + head_off;
-  const int star = fused ? L + T0 % p.window : -1;
+  const int star = fused ? L + f.T0 % p.window : -1;
   const S *kn = fused ? static_cast<const S *>(p.k_new) + bh * D : nullptr;
   const S *vn = fused ? static_cast<const S *>(p.v_new) + bh * D : nullptr;
 
@@ -383,7 +378,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
       o = fmaf(a, sm_acc[w2][threadIdx.x], o);
       lsum = fmaf(a, sm_l[w2], lsum);
     }
-    if (p.one_launch) {
+    if (write_out) {
       store_out<E>(p.out, bh * D + threadIdx.x, o / lsum);  // what the merge of one split computes
     } else {
       po[threadIdx.x] = o;
@@ -393,13 +388,169 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
       }
     }
   }
+  __syncthreads();  // the LDS above may be reused by the caller's next range
+}
+
+// Split-K decode. Grid (H, B, splits), 4 waves. Workgroup (b, h, sp) owns the
+// key slots [sp*chunk, min(vis, (sp+1)*chunk)) of (b, h), vis = L_m + min(n, T).
+template <class E, int D, int U>
+__global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
+  const int b = blockIdx.y, h = blockIdx.x, sp = blockIdx.z;
+  const int64_t bh = (int64_t)b * p.heads + h;
+  float *po = p.part_o + (bh * p.splits + sp) * D;
+  float *pml = p.part_ml + (bh * p.splits + sp) * 2;
+  const bool fused = p.k_new != nullptr;
+  const SeqFacts f = seq_facts<Geometry<E, D>::kEpl>(p, b);
+  if (sp == 0 && h == 0 && threadIdx.x == 0) {
+    p.seq_state[b] = (f.err || !fused) ? -1 : f.T0 + 1;
+    if (f.err) atomicOr(p.error, f.err);
+  }
+
+  const int start = sp * p.chunk;
+  const int end = min(f.vis, start + p.chunk);
+  if (f.err || start >= end) {  // empty partial state (one launch: a zero output)
+    if (p.one_launch) {
+      for (int i = threadIdx.x; i < D; i += 256) store_out<E>(p.out, bh * D + i, 0.f);
+      return;
+    }
+    for (int i = threadIdx.x; i < D; i += 256) po[i] = 0.f;
+    if (threadIdx.x == 0) {
+      pml[0] = kNegInf;
+      pml[1] = 0.f;
+    }
+    return;
+  }
+  attend_range<E, D, U>(p, b, h, f, start, end, po, pml, p.one_launch != 0);
   // One fused launch: every workgroup of sequence b read step[b] before it
   // counts itself here, so the last of the H may publish the new step.
   if (p.one_launch && fused && threadIdx.x == 0) {
     if (atomicAdd(&p.arrive[b], 1) == p.heads - 1) {
       atomicExch(&p.arrive[b], 0);
-      p.step[b] = T0 + 1;
+      p.step[b] = f.T0 + 1;
     }
+  }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int64_t wave_inclusive_sum(int64_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Flat work list (a ragged batch). The visible slots of every (sequence, head),
+// in order (b, h), form one list of T_all = H * sum_b vis_b slots; workgroup g
+// of the G in the grid attends over slots [T_all g / G, T_all (g + 1) / G), so
+// every workgroup streams the same number of bytes whatever the lengths. A
+// workgroup may cover the end of one (sequence, head) and the start of the next:
+// it writes one partial state per (sequence, head) it touches, at index g + s
+// (s = b H + h), unique because a later workgroup never touches an earlier
+// (sequence, head). Workgroup 0 also publishes the per-sequence prefix sums
+// (seq_pre[b] = sum of vis over sequences before b, seq_pre[B] = the total), the
+// new step counts for the merge, and the error bits.
+template <class E, int D, int U>
+__global__ __launch_bounds__(256) void decode_flat_kernel(DecodeParams p) {
+  constexpr int kEpl = Geometry<E, D>::kEpl;
+  const int lane = threadIdx.x & 63;
+  const int gi = blockIdx.x, G = gridDim.x;
+  const int B = p.batch, H = p.heads;
+  const bool fused = p.k_new != nullptr;
+
+  int64_t total = 0;  // sum of vis over the batch (every wave computes it)
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    int64_t vis = 0;
+    if (b < B) {
+      const SeqFacts f = seq_facts<kEpl>(p, b);
+      vis = f.vis;
+      if (gi == 0 && threadIdx.x < 64) {
+        p.seq_state[b] = (f.err || !fused) ? -1 : f.T0 + 1;
+        if (f.err) atomicOr(p.error, f.err);
+      }
+    }
+    const int64_t incl = wave_inclusive_sum(vis);
+    if (gi == 0 && threadIdx.x < 64 && b < B) p.seq_pre[b] = total + incl - vis;
+    total += __shfl(incl, 63, 64);
+  }
+  if (gi == 0 && threadIdx.x == 0) p.seq_pre[B] = total;
+
+  const int64_t t_all = total * H;
+  const int64_t lo = t_all * gi / G, hi = t_all * (gi + 1) / G;
+  if (lo >= hi) return;  // an empty piece (the whole workgroup)
+
+  // The sequence holding slot lo of the list: the first b whose prefix end
+  // H * (pre_b + vis_b) exceeds lo.
+  int b = 0;
+  int64_t pre = 0;  // sum of vis before sequence b
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int bb = b0 + lane;
+    const int64_t vis = bb < B ? (int64_t)seq_facts<kEpl>(p, bb).vis : 0;
+    const int64_t incl = wave_inclusive_sum(vis);
+    const uint64_t past = __ballot((pre + incl) * H > lo && bb < B);
+    if (past != 0) {
+      const int first = __ffsll((unsigned long long)past) - 1;
+      b = b0 + first;
+      pre += __shfl(incl - vis, first, 64);
+      break;
+    }
+    pre += __shfl(incl, 63, 64);
+  }
+
+  // Walk the (sequence, head) ranges of [lo, hi).
+  int64_t pos = lo;
+  while (pos < hi && b < B) {
+    const SeqFacts f = seq_facts<kEpl>(p, b);
+    const int64_t seq0 = pre * H;  // first list slot of sequence b
+    if (f.vis > 0 && pos < seq0 + (int64_t)f.vis * H) {
+      const int h = (int)((pos - seq0) / f.vis);
+      const int start = (int)((pos - seq0) - (int64_t)h * f.vis);
+      const int end = (int)min((int64_t)f.vis, start + (hi - pos));
+      const int64_t idx = gi + (int64_t)b * H + h;
+      attend_range<E, D, U>(p, b, h, f, start, end, p.part_o + idx * D, p.part_ml + idx * 2, false);
+      pos += end - start;
+    } else {
+      pre += f.vis;
+      ++b;
+    }
+  }
+}
+
+// Merge of the flat work list: grid (H, B), D threads. The list slots of
+// (sequence b, head h) are [S, S + vis) with S = H pre_b + h vis; the workgroups
+// that covered them are g0 .. g1 (those whose piece [T_all g / G, T_all (g+1) / G)
+// is not empty), their partial states at g + b H + h.
+template <class E, int D>
+__global__ __launch_bounds__(128) void decode_merge_flat_kernel(DecodeParams p) {
+  const int b = blockIdx.y, h = blockIdx.x, col = threadIdx.x;
+  const int H = p.heads;
+  const int64_t G = p.flat_wgs;
+  const int64_t bh = (int64_t)b * H + h;
+  const int64_t pre = p.seq_pre[b], vis = p.seq_pre[b + 1] - pre;
+  const int64_t t_all = p.seq_pre[p.batch] * H;
+  float o = 0.f;
+  if (vis > 0) {
+    const int64_t S = pre * H + (int64_t)h * vis;
+    const int64_t g0 = ((S + 1) * G - 1) / t_all, g1 = ((S + vis) * G - 1) / t_all;
+    float M = kNegInf;
+    for (int64_t g = g0; g <= g1; ++g)
+      if (t_all * g / G < t_all * (g + 1) / G) M = fmaxf(M, p.part_ml[(g + bh) * 2]);
+    float num = 0.f, den = 0.f;
+    for (int64_t g = g0; g <= g1; ++g) {
+      if (t_all * g / G == t_all * (g + 1) / G) continue;  // empty piece: wrote nothing
+      const float w = __builtin_amdgcn_exp2f(p.part_ml[(g + bh) * 2] - M);
+      num = fmaf(w, p.part_o[(g + bh) * D + col], num);
+      den = fmaf(w, p.part_ml[(g + bh) * 2 + 1], den);
+    }
+    o = num / den;
+  }
+  store_out<E>(p.out, bh * D + col, o);
+  if (h == 0 && col == 0 && p.k_new != nullptr) {
+    const int32_t next = p.seq_state[b];
+    if (next >= 0) p.step[b] = next;
   }
 }
 
@@ -438,6 +589,13 @@ hipError_t launch_decode_t(const DecodeParams &p, hipStream_t s) {
   // Heads fastest: workgroup i lands on XCD i mod 8, so every sequence's chunks
   // spread over all XCDs whatever the split count (in a ragged batch the later
   // chunks are often empty; with splits fastest they would pile onto a few XCDs).
+  if (p.flat_wgs > 0) {
+    hipLaunchKernelGGL((decode_flat_kernel<E, D, kU>), dim3(p.flat_wgs), dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_merge_flat_kernel<E, D>), dim3(p.heads, p.batch), dim3(D), 0, s, p);
+    return hipGetLastError();
+  }
   dim3 grid(p.heads, p.batch, p.splits);
   hipLaunchKernelGGL((decode_split_kernel<E, D, kU>), grid, dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();

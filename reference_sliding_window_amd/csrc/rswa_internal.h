@@ -9,25 +9,30 @@
 namespace rswa {
 
 // Work split of one decode launch: every (sequence, head) is cut into `splits`
-// chunks of `chunk` key slots; each chunk is one workgroup.
+// chunks of `chunk` key slots, each chunk one workgroup; or, when flat_wgs > 0,
+// the visible slots of all (sequence, head) pairs form one list cut into
+// flat_wgs equal pieces, one per workgroup.
 struct SplitPlan {
   int32_t splits;
   int32_t chunk;
+  int32_t flat_wgs;
 };
 
 // Chooses the split plan from host-known sizes only (the per-sequence lengths
 // live on the device). requested = 0 selects the library's choice.
 SplitPlan plan_decode_splits(int32_t batch, int32_t heads, int32_t max_len, int32_t requested);
 
-// Byte layout of the decode workspace.
+// Byte layout of the decode workspace. Partial states: [B*H][splits] for
+// per-(sequence, head) chunks, [flat_wgs + B*H] for the flat list.
 struct WorkspaceLayout {
-  size_t part_o;     // float [B*H][splits][d]: unnormalised partial outputs
-  size_t part_ml;    // float [B*H][splits][2]: running max (base 2) and sum
+  size_t part_o;     // float [units][d]: unnormalised partial outputs
+  size_t part_ml;    // float [units][2]: running max (base 2) and sum
   size_t seq_state;  // int32 [B]: new step value for the merge pass, or -1
+  size_t seq_pre;    // int64 [B + 1]: flat list, visible slots before sequence b
   size_t total;
 };
 WorkspaceLayout decode_workspace_layout(int32_t batch, int32_t heads, int32_t head_dim,
-                                        int32_t splits);
+                                        const SplitPlan &plan);
 
 struct DecodeParams {
   const void *q;
@@ -43,6 +48,7 @@ struct DecodeParams {
   float *part_o;
   float *part_ml;
   int32_t *seq_state;
+  int64_t *seq_pre;  // flat list only
   // One launch (splits == 1 and, for a fused call, arrival counters given): the
   // split kernel writes out itself; the last of a sequence's H workgroups to
   // count itself in arrive[b] publishes step[b] and sets arrive[b] back to 0.
@@ -50,6 +56,7 @@ struct DecodeParams {
   int32_t one_launch;
   int32_t batch, heads, window, max_ref_len;
   int32_t splits, chunk;
+  int32_t flat_wgs;  // > 0: flat work list over this many workgroups
   float scale_log2;  // softmax scale * log2(e)
 };
 

@@ -110,16 +110,25 @@ def test_workspace_grows_with_splits():
 
 def test_library_split_choice():
     """One chunk per (sequence, head) -- one launch -- for a batch that fills the GPU with
-    sequences of at most 12288 slots; split chunks otherwise."""
+    sequences of at most 12288 slots; otherwise a flat work list for large steps and
+    short per-(sequence, head) chunks for small ones."""
     ws = lambda s, **kw: rs.rswa_decode_workspace_size(good_desc(**kw), s)
     forty = dict(batch=32, num_heads=16, max_ref_len=10272, window=128)
     assert ws(0, **forty) == ws(1, **forty)
     one_page = dict(batch=1, num_heads=16, max_ref_len=288, window=128)
     assert ws(0, **one_page) > ws(1, **one_page)
+    # a large step (>= 4M slots of capacity) not decoded in one launch: the flat work
+    # list over 512 workgroups, partial states for 512 + B*H (sequence, head) pieces
+    r256 = lambda x: (x + 255) // 256 * 256
+    flat = lambda B, H: r256((512 + B * H) * 128 * 4) + r256((512 + B * H) * 8) + r256(B * 4) + r256((B + 1) * 8)
     ragged = dict(batch=64, num_heads=16, max_ref_len=12832, window=128)
-    assert ws(0, **ragged) == ws(7, **ragged)  # chunks of at most 2048 slots
-    few = dict(batch=2, num_heads=16, max_ref_len=10272, window=128)
-    assert ws(0, **few) > ws(8, **few)
+    assert ws(0, **ragged) == flat(64, 16) < ws(7, **ragged)
+    contrast = dict(batch=32, num_heads=16, max_ref_len=10272, window=6144)
+    assert ws(0, **contrast) == flat(32, 16)
+    few = dict(batch=2, num_heads=16, max_ref_len=10272, window=128)   # 333K slots: chunks
+    assert ws(0, **few) > ws(8, **few) and ws(0, **few) != flat(2, 16)
+    # small steps keep per-(sequence, head) chunks: one page, 16 heads -> 7 chunks of 64 slots
+    assert ws(0, **one_page) == ws(7, **one_page)
 
 
 def test_append_and_init_argument_checks():

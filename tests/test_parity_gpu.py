@@ -19,6 +19,8 @@ import oracle.pool as opool
 from gpu_util import (DecodeRun, bits, check_close, oracle_decode_all_pairs, shared_decode_inputs,
                       storage_bits, to_dev, to_f64)
 
+DTYPE = {"bf16": rs.RSWA_BF16, "fp32": rs.RSWA_FP32}
+
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
@@ -114,6 +116,91 @@ def test_forty_page_full_attention_contrast():
     for T in checks:
         ma, rel = check_close(got[T], ref[T], "bf16", f"contrast T={T}")
         print(f"contrast T={T}: max|d|={ma:.3e} worst (b,h) rel={rel:.3e}", flush=True)
+
+
+def _flat_workspace_bytes(B, H, d):
+    r256 = lambda x: (x + 255) // 256 * 256
+    return r256((512 + B * H) * d * 4) + r256((512 + B * H) * 8) + r256(B * 4) + r256((B + 1) * 8)
+
+
+@pytest.mark.parametrize("dtype,d,B,H,max_L,n,fused,seed", [
+    ("bf16", 128, 70, 4, 15000, 128, True, 31),
+    ("fp32", 64, 130, 3, 11000, 16, True, 32),
+    ("bf16", 128, 3, 16, 90000, 128, False, 33),
+    ("bf16", 64, 200, 2, 11000, 8, True, 34),
+])
+def test_flat_work_list_ragged_batches(dtype, d, B, H, max_L, n, fused, seed):
+    """The flat work list (the library's plan for large steps not decoded in one launch):
+    sequences of very different lengths -- empty references, a window not yet full,
+    wrapped rings -- and one sequence flagged invalid; every (sequence, head) of the
+    step against the oracle, the new token's slot bit for bit, the step counters."""
+    rng = np.random.default_rng(seed)
+    L = rng.integers(0, max_L + 1, size=B)
+    L[0], L[-1] = 0, max_L
+    T_now = rng.integers(1, 3 * n, size=B)          # the step's output index (1-based)
+    bad = B // 2
+    banner(f"flat work list {dtype} d={d} B={B} H={H} L {L.min()}..{L.max()} n={n} fused={fused}")
+    cache = rs.KVCache.allocate(L.tolist(), H, d, n, dtype=DTYPE[dtype])
+    assert rs.rswa_decode_workspace_size(cache.desc, 0) == _flat_workspace_bytes(B, H, d)
+    dt = np.uint16 if dtype == "bf16" else np.float32
+    host_k = np.zeros(cache.k.numel(), dtype=dt)
+    host_v = np.zeros(cache.v.numel(), dtype=dt)
+    bases = cache.seq_base.cpu().numpy()
+    draw = lambda *words, shape: wl.draw(dtype, 1.0, shape, 20269000 + seed, *words)
+    q = draw(0, shape=(B, H, d))
+    k_new = draw(1, shape=(B, H, d))
+    v_new = draw(2, shape=(B, H, d))
+    refs, wins = [], []
+    for b in range(B):
+        Lb, T = int(L[b]), int(T_now[b])
+        kr, vr = draw(3, b, shape=(H, Lb, d)), draw(4, b, shape=(H, Lb, d))
+        blk_k = host_k[bases[b]:bases[b] + H * (Lb + n) * d].reshape(H, Lb + n, d)
+        blk_v = host_v[bases[b]:bases[b] + H * (Lb + n) * d].reshape(H, Lb + n, d)
+        blk_k[:, :Lb], blk_v[:, :Lb] = kr, vr
+        win = {t: (draw(5, b, t, shape=(H, d)), draw(6, b, t, shape=(H, d))) for t in range(max(1, T - n), T)}
+        win[T] = (k_new[b], v_new[b])
+        last = T if not fused else T - 1          # outputs already in the cache before the call
+        for t in range(max(1, last - n + 1), last + 1):
+            blk_k[:, orc.ring_slot(Lb, n, t)], blk_v[:, orc.ring_slot(Lb, n, t)] = win[t]
+        refs.append((kr, vr))
+        wins.append(win)
+    cache.k.copy_(to_dev(host_k, dtype))
+    cache.v.copy_(to_dev(host_v, dtype))
+    steps0 = (T_now - 1 if fused else T_now).astype(np.int32)
+    cache.step.copy_(torch.from_numpy(steps0))
+    cache.ref_len[bad] = max_L + 1                    # above max_ref_len: flagged and skipped
+    ws = cache.workspace()
+    out = torch.full((B, H, d), float("nan"), dtype=cache.k.dtype, device="cuda")
+    kd, vd = (to_dev(k_new, dtype), to_dev(v_new, dtype)) if fused else (None, None)
+    rs.rswa_decode_attn(cache.desc, to_dev(q, dtype), out, kd, vd, 0.0, 0, ws)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    assert rs.rswa_check_device_error(cache.desc) == rs.RSWA_DEVERR_REF_LEN
+    steps = cache.step.cpu().numpy()
+    expect_steps = T_now.astype(np.int32).copy()
+    expect_steps[bad] = steps0[bad]
+    assert np.array_equal(steps, expect_steps)
+    assert np.all(got[bad] == 0)
+    good = [b for b in range(B) if b != bad]
+    ref = np.zeros((len(good), H, d))
+    for i, b in enumerate(good):
+        Lb, T = int(L[b]), int(T_now[b])
+        first = max(1, T - n + 1)
+        ko = np.stack([wins[b][t][0] for t in range(first, T + 1)], axis=1)
+        vo = np.stack([wins[b][t][1] for t in range(first, T + 1)], axis=1)
+        kr, vr = refs[b]
+        for h in range(H):
+            ref[i, h] = orc.decode_output(wl.to_f64(q[b, h], dtype), wl.to_f64(kr[h], dtype),
+                                          wl.to_f64(vr[h], dtype), wl.to_f64(ko[h], dtype),
+                                          wl.to_f64(vo[h], dtype), first, Lb, n, T, 1.0 / math.sqrt(d))
+    ma, rel = check_close(got[good], ref, dtype, "flat work list")
+    print(f"flat work list: max|d|={ma:.3e} worst (b,h) rel={rel:.3e}")
+    if fused:   # the new token sits in its ring slot, bit for bit (flagged sequence untouched)
+        kb_all = bits(cache.k)
+        for b in good:
+            Lb, T = int(L[b]), int(T_now[b])
+            blk = kb_all[bases[b]:bases[b] + H * (Lb + n) * d].reshape(H, Lb + n, d)
+            assert np.array_equal(blk[:, orc.ring_slot(Lb, n, T)], storage_bits(k_new[b]))
 
 
 def test_ragged_batch_one_fused_step():
