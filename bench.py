@@ -120,6 +120,10 @@ def cpu_baseline(w, kref, vref, T):
                       f"host reports {len(os.sched_getaffinity(0))} cores available"}
 
 
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def device_facts(torch):
     p = torch.cuda.get_device_properties(0)
     return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
@@ -137,6 +141,17 @@ def probe_read_GBps(torch, rs, stream, nbytes=4 << 30):
     ms = event_time_ms(run, 10, stream) / 10
     del buf, sink
     return nbytes / (ms * 1e-3) / 1e9
+
+
+def mfma_probe_tflops(torch, rs, stream, iters=4096, workgroups=512):
+    """bf16 32x32x16 matrix products issued back to back by two waves per SIMD: the rate the chip
+    sustains at the clock it holds under matrix load (the packed kernels' practical ceiling)."""
+    sink = torch.empty(workgroups, dtype=torch.float32, device="cuda")
+    run = lambda i: rs.rswa_probe_mfma(sink, workgroups, iters, stream=stream)
+    for _ in range(3):
+        run(0)
+    ms = event_time_ms(run, 10, stream) / 10
+    return workgroups * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12
 
 
 def gemm_tflops(torch, stream, m=8192):
@@ -297,6 +312,7 @@ def main():
         step(i)
     torch.cuda.synchronize()
     t_first = fill + W + 1                       # output index T of the first timed step
+    progress(f"window filled and {W} warm-up steps run; timing {K} steps")
     ms = event_time_ms(lambda i: step(fill + W + i), K, stream)
     ms_per_step = ms / K
     # the same number of further steps, each between its own pair of events
@@ -352,6 +368,7 @@ def main():
     }
     del qs, ks, vs
 
+    progress("contract line measured")
     if not args.no_secondary:
         # full-attention contrast: the same kernels over a cache of exactly L_m + T slots (window T,
         # every output kept), attend-only at output T
@@ -377,6 +394,7 @@ def main():
             "full_attention_per_T": contrast,
             "rswa_attend_only_ms": ms_r,
             "rswa_fused_step_ms": ms_per_step}
+        progress("full-attention contrast measured")
         # ragged batch: 64 sequences, each with its own pages and decode position, one fused step
         rw = wl.RAGGED_64
         rdraw = wl.ragged_lengths(rw)
@@ -411,7 +429,9 @@ def main():
                     "decode position (pages ~ U{1..50}, T ~ U{1..8192}); no state restored in between"}
         del rc, rq, rk, rv, rout, rws
 
+        progress("ragged batch measured")
         gemm = gemm_tflops(torch, stream)
+        mfma_rate = mfma_probe_tflops(torch, rs, stream)
         # packed 32K masked forward (matrix cores)
         mw = wl.PACKED_32K
         Q, Kp, Vp = wl.packed_qkv(mw)
@@ -429,7 +449,8 @@ def main():
                               mode == rs.RSWA_PREFIX_FULL)
             masked[name] = {"ms": ms_m, "algorithmic_flop": fl, "TFLOPs": fl / (ms_m * 1e-3) / 1e12,
                             "frac_of_bf16_peak": fl / (ms_m * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                            "frac_of_measured_gemm": fl / (ms_m * 1e-3) / 1e12 / gemm}
+                            "frac_of_measured_gemm": fl / (ms_m * 1e-3) / 1e12 / gemm,
+                            "frac_of_measured_mfma_rate": fl / (ms_m * 1e-3) / 1e12 / mfma_rate}
         # packed 32K backward (dQ, dK, dV) of the causal-prefix forward
         Gd = to_d(wl.packed_dout(mw))
         lse = torch.empty((mw.heads, mw.seq_len), dtype=torch.float32, device="cuda")
@@ -448,6 +469,7 @@ def main():
         masked["backward_prefix_causal"] = {
             "ms": ms_b, "algorithmic_flop": fl_b, "TFLOPs": fl_b / (ms_b * 1e-3) / 1e12,
             "frac_of_bf16_peak": fl_b / (ms_b * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "frac_of_measured_mfma_rate": fl_b / (ms_b * 1e-3) / 1e12 / mfma_rate,
             "flop_convention": "2.5x the forward: five products of 2 d flop per visible pair (S, dP, dV, dK, "
                                "dQ); the kernels execute seven (S and dP are formed in both the dQ and "
                                "the dK/dV pass)",
@@ -455,10 +477,14 @@ def main():
         del ws_b
         result["masked_32k"] = {"workload": mw.name, "seq_len": mw.seq_len, "ref_len": mw.ref_len,
                                 "window": mw.window, "heads": mw.heads,
-                                "measured_bf16_gemm_TFLOPs": gemm, "gemm": "8192^3 bf16 torch.matmul", **masked}
+                                "measured_bf16_gemm_TFLOPs": gemm, "gemm": "8192^3 bf16 torch.matmul",
+                                "measured_mfma_rate_TFLOPs": mfma_rate,
+                                "mfma_rate": "rswa_probe_mfma: 32x32x16 bf16 products back to back, two waves "
+                                             "per SIMD, nothing else in the loop", **masked}
         if not args.no_cpu_baseline:
             result["cpu_baseline_masked"] = cpu_masked_rows(mw, Q, Kp, Vp)
 
+        progress("packed 32K forward and backward measured")
         # several documents per 32K pack (samples independent), forward on matrix cores
         cu, refs = wl.varlen_pack_layout(mw.seq_len, mw.base_seed)
         lens = np.diff(cu)
@@ -498,6 +524,7 @@ def main():
                                   "for the single-sequence backward"}}
         del Qd, Kd, Vd, Od, cu_d, refs_d, Gd, dq, dk, dv, lse, ws_v
 
+        progress("10-document pack measured")
         # prefill -> decode hand-off at the 40-page decode shape: B sequences of L_m reference
         # rows plus T0 = n outputs (the window full at hand-off), one call for the whole batch
         T0 = n
@@ -534,6 +561,7 @@ def main():
                     "forward_only_ms is the same pack through rswa_masked_attn_varlen"}
         del pq, pk, pv, pout, pcache
 
+        progress("prefill measured")
         # a decode step through `layers` attention layers (own cache each) as one HIP graph, at the
         # output lengths of the pages' TPS table, R-SWA against full attention (attention share only)
         layers = args.layers
@@ -593,6 +621,7 @@ def main():
             "rswa_fused_step_ms": ms_rf, "rswa_fused_tokens_per_s": B / (ms_rf * 1e-3)}
         del r_caches, ws_r, gq, gk, gv, gout
 
+        progress("multi-layer graph measured")
         # one-page decode (B = 1): 3.4 MB per step, a working set the caches hold, so the step is
         # bound by launch and kernel latency; fused append + attend steps eagerly and replayed as a
         # one-layer HIP graph, past the window fill (T > n)
@@ -662,8 +691,10 @@ def main():
         del oc, oq, ok_, ov, oout, ows, lcs, lq, lk, lv, lo
 
     if args.curve:
+        progress("per-step curve")
         result["per_step_curve"] = per_step_curve(torch, rs, w, stream, w.steps)
     if not args.no_cpu_baseline:
+        progress("CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(w, kref, vref, t_first + K - 1)
     result["setup_s"] = setup_s
     print(json.dumps(result), flush=True)

@@ -398,6 +398,10 @@ RSWA_API rswa_status_t rswa_masked_attn_bwd_varlen(
  * The captured work holds no memset nodes, only the decode kernels. Replays
  * of one graph, and replays of graphs that share caches or workspace, must
  * not run concurrently.
+ * Use it for several layers: one replay costs more host and launch time than
+ * the one or two kernel launches of a single eager call (one layer of a
+ * one-page step: 14 us replayed against 8 us eagerly; 12 layers: 87 us against
+ * 96 us).
  */
 typedef struct rswa_decode_graph rswa_decode_graph_t;
 
@@ -420,6 +424,17 @@ RSWA_API rswa_status_t rswa_decode_graph_destroy(rswa_decode_graph_t *graph);
  */
 RSWA_API rswa_status_t rswa_probe_stream_read(const void *buf, size_t bytes, float *sink,
                                      int32_t workgroups, void *stream);
+
+/*
+ * Measurement helper, not part of the attention path: `workgroups` workgroups
+ * of 4 waves (0 picks 512, two waves per SIMD on 256 CUs) each run `iters`
+ * rounds of 4 independent v_mfma_f32_32x32x16_bf16 products (the packed
+ * kernels' instruction; 32768 FLOP each) and write one value per workgroup to
+ * `sink` (device float [workgroups]). FLOP = workgroups * 4 waves * iters * 4 *
+ * 32768; timing it gives the matrix-core rate the chip sustains at the clock it
+ * holds under matrix load, the practical ceiling of the packed kernels.
+ */
+RSWA_API rswa_status_t rswa_probe_mfma(float *sink, int32_t workgroups, int32_t iters, void *stream);
 
 /*
  * Synchronise `stream`, read the cache's device error word into *flags

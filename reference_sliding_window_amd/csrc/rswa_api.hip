@@ -676,6 +676,15 @@ rswa_status_t rswa_probe_stream_read(const void *buf, size_t bytes, float *sink,
   return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
 }
 
+rswa_status_t rswa_probe_mfma(float *sink, int32_t workgroups, int32_t iters, void *stream) {
+  if (sink == nullptr) return RSWA_ERR_NULL;
+  if (workgroups < 0 || iters < 1) return RSWA_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return RSWA_ERR_ALIGN;
+  const hipError_t e = launch_probe_mfma(sink, workgroups == 0 ? 512 : workgroups, iters,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
+}
+
 rswa_status_t rswa_check_device_error(const rswa_cache_t *cache, int32_t *flags, void *stream) {
   if (cache == nullptr || cache->error == nullptr || flags == nullptr) return RSWA_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);

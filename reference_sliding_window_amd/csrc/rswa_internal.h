@@ -159,5 +159,6 @@ BwdPlan plan_masked_bwd(int32_t seq_len, int32_t ref_len, int32_t heads, int32_t
 hipError_t launch_masked_bwd(const MaskedBwdParams &p, hipStream_t s);
 hipError_t launch_clear_word(int32_t *word, hipStream_t s);
 hipError_t launch_probe_read(const void *buf, size_t bytes, float *sink, int32_t workgroups, hipStream_t s);
+hipError_t launch_probe_mfma(float *sink, int32_t workgroups, int32_t iters, hipStream_t s);
 
 }  // namespace rswa

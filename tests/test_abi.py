@@ -233,6 +233,14 @@ def test_probe_argument_checks():
     assert pr(nbytes=0) == rs.RSWA_OK
 
 
+def test_probe_mfma_argument_checks():
+    pm = lambda **kw: rs.rswa_probe_mfma(**{**dict(sink=A, workgroups=0, iters=16), **kw}, check=False)
+    assert pm(sink=None) == rs.RSWA_ERR_NULL
+    assert pm(workgroups=-1) == rs.RSWA_ERR_SHAPE
+    assert pm(iters=0) == rs.RSWA_ERR_SHAPE
+    assert pm(sink=A + 2) == rs.RSWA_ERR_ALIGN
+
+
 def test_masked_bwd_workspace_size():
     ws = rs.rswa_masked_bwd_workspace_size
     assert ws(-1, 0, 2) == 0
