@@ -130,3 +130,58 @@ def test_attend_only_graph_keeps_steps_and_repeats():
             assert caches[l].step.cpu().tolist() == [5, 5]
     finally:
         rs.rswa_decode_graph_destroy(g)
+
+
+def test_graph_replays_equal_eager_steps_flat_work_list():
+    """A ragged batch large enough for the flat work list (flat kernel + merge per layer):
+    every replay gives the eager calls' bits, step counters and cache images, through the
+    window's wrap. (The flat path's outputs are checked against the oracle elsewhere.)"""
+    refs, H, d, n, L, steps = [33000, 0, 100, 5000], 32, 128, 16, 2, 20
+    B = len(refs)
+    banner(f"decode graph vs eager, flat work list, refs {refs} H={H}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(8300)
+    pools = []
+    for _ in range(2):          # eager, graphed: identical initial caches
+        cs = []
+        for l in range(L):
+            c = rs.KVCache.allocate(refs, H, d, n, dtype=rs.RSWA_BF16)
+            cs.append(c)
+        pools.append(cs)
+    for l in range(L):
+        k0 = torch.randn(pools[0][l].k.shape, device="cuda", generator=gen).to(torch.bfloat16)
+        v0 = torch.randn(pools[0][l].v.shape, device="cuda", generator=gen).to(torch.bfloat16)
+        for cs in pools:
+            cs[l].k.copy_(k0)
+            cs[l].v.copy_(v0)
+            cs[l].step.zero_()
+    eager, graphed = pools
+    assert rs.rswa_decode_workspace_size(eager[0].desc, 0) == rs.rswa_workspace_size(B, H, d, max(refs) + n)
+    ws_e, ws_g = eager[0].workspace(), graphed[0].workspace()
+    sq = [torch.zeros((B, H, d), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    sk = [torch.zeros_like(x) for x in sq]
+    sv = [torch.zeros_like(x) for x in sq]
+    sout = [torch.zeros_like(x) for x in sq]
+    _, g = rs.rswa_decode_graph_create([c.desc for c in graphed], sq, sout, sk, sv, workspace=ws_g)
+    out_e = torch.empty((B, H, d), dtype=torch.bfloat16, device="cuda")
+    try:
+        for i in range(steps):
+            x = [[torch.randn((B, H, d), device="cuda", generator=gen).to(torch.bfloat16) for _ in range(3)]
+                 for _ in range(L)]
+            outs_e = []
+            for l in range(L):
+                rs.rswa_decode_attn(eager[l].desc, x[l][0], out_e, x[l][1], x[l][2], 0.0, 0, ws_e)
+                outs_e.append(bits(out_e))
+            for l in range(L):
+                sq[l].copy_(x[l][0]); sk[l].copy_(x[l][1]); sv[l].copy_(x[l][2])
+            rs.rswa_decode_graph_launch(g)
+            torch.cuda.synchronize()
+            for l in range(L):
+                assert np.array_equal(bits(sout[l]), outs_e[l]), f"step {i + 1} layer {l}"
+        for l in range(L):
+            assert graphed[l].step.cpu().tolist() == eager[l].step.cpu().tolist() == [steps] * B
+            assert np.array_equal(bits(graphed[l].k), bits(eager[l].k))
+            assert np.array_equal(bits(graphed[l].v), bits(eager[l].v))
+            assert rs.rswa_check_device_error(graphed[l].desc) == 0
+    finally:
+        rs.rswa_decode_graph_destroy(g)
