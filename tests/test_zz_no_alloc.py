@@ -61,3 +61,41 @@ def test_noalloc_rejects_more_than_its_buffer():
     out = torch.empty_like(q)
     st = rs.rswa_decode_attn_noalloc(cache.desc, q, out, None, None, 0.0, 64, check=False)
     assert st == rs.RSWA_ERR_WORKSPACE
+
+
+def test_noalloc_under_graph_capture():
+    """The caller it is for: a decode step captured into a HIP graph (torch.cuda.graph), so
+    the call may not allocate. Every replay, with the program's own eager work between
+    replays, gives the bits of the eager no-alloc call on an identical cache; both run on
+    one stream, so they never overlap on the shared buffer."""
+    w = wl.DecodeWorkload("noalloc-graph", batch=4, heads=16, head_dim=128, ref_len=3000, window=128,
+                          steps=12, dtype="bf16", sigma_q=1.0, sigma_kv=1.0, base_seed=8104)
+    print("\n[case] noalloc under graph capture", flush=True)
+    eager = DecodeRun(w)
+    graphed = DecodeRun(w, ref=(eager.kref, eager.vref))
+    sq, sk, sv = (torch.zeros((w.batch, w.heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+                  for _ in range(3))
+    sout = torch.zeros_like(sq)
+    out_e = torch.empty_like(sq)
+    q, k, v = wl.steps_qkv(w, 1, w.steps)
+    # step 1 eagerly on both caches (also the library's first call on this device, outside capture)
+    for r in (eager, graphed):
+        rs.rswa_decode_attn_noalloc(r.cache.desc, to_dev(q[0], "bf16"), r.out, to_dev(k[0], "bf16"),
+                                    to_dev(v[0], "bf16"))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rs.rswa_decode_attn_noalloc(graphed.cache.desc, sq, sout, sk, sv)
+    other = torch.randn(1 << 20, device="cuda")
+    for T in range(2, w.steps + 1):
+        qd, kd, vd = (to_dev(x[T - 1], "bf16") for x in (q, k, v))
+        rs.rswa_decode_attn_noalloc(eager.cache.desc, qd, out_e, kd, vd)
+        sq.copy_(qd); sk.copy_(kd); sv.copy_(vd)
+        g.replay()
+        other.mul_(1.0001)                  # the program's own eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(sout), bits(out_e)), f"step {T}"
+    assert eager.cache.step.cpu().tolist() == graphed.cache.step.cpu().tolist() == [w.steps] * w.batch
+    assert np.array_equal(bits(eager.cache.k), bits(graphed.cache.k))
+    assert np.array_equal(bits(eager.cache.v), bits(graphed.cache.v))
+    assert rs.rswa_check_device_error(graphed.cache.desc) == 0
