@@ -193,7 +193,11 @@ RSWA_API size_t rswa_decode_workspace_size(const rswa_cache_t *cache, int32_t nu
  * publishes step[b] and sets arrive[b] back to 0. arrive must hold zeros before
  * the first call (rswa_cache_init zeroes it) and is zero again after every
  * call. The library picks one split when every sequence fits one chunk of a
- * batch that fills the GPU.
+ * batch that fills the GPU. With num_splits = 0 and a large step that does not
+ * qualify (batch * heads * (max_ref_len + window) >= 2^22 slots, e.g. a ragged
+ * batch), it instead cuts the visible slots of all (sequence, head) pairs,
+ * counted on the device, into equal pieces, one per workgroup, and merges the
+ * pieces' partial states per pair (a work-list kernel and a merge kernel).
  */
 RSWA_API rswa_status_t rswa_decode_attn(const rswa_cache_t *cache, const void *q, void *out,
                                const void *k_new, const void *v_new, float scale,
