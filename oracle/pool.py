@@ -138,7 +138,10 @@ class OraclePool:
         return self
 
     def __exit__(self, *exc):
-        self._pool.terminate() if exc[0] is not None else self.close()
+        if exc[0] is not None:
+            self._pool.terminate()   # a failed map: do not wait on workers still busy
+        else:
+            self.close()
 
 
 def pool_map(fn, tasks, arrays: SharedArrays | None = None, processes: int | None = None,
