@@ -369,8 +369,12 @@ class KVCache:
             off += heads * (L + window) * head_dim
             off = (off + align - 1) // align * align
         tdt = _TORCH_DTYPE[dtype]
-        k = torch.empty(max(off, align), dtype=tdt, device=device)
-        v = torch.empty(max(off, align), dtype=tdt, device=device)
+        # zero-filled: slots no call has written yet (a window not yet full,
+        # alignment gaps) hold zeros, not whatever the allocator handed back, so
+        # two caches driven alike compare equal bit for bit and checkpoints of
+        # the pools are reproducible
+        k = torch.zeros(max(off, align), dtype=tdt, device=device)
+        v = torch.zeros(max(off, align), dtype=tdt, device=device)
         seq_base = torch.tensor(bases, dtype=torch.int64, device=device)
         ref_len = torch.tensor(ref_lens, dtype=torch.int32, device=device)
         step = torch.zeros(len(ref_lens), dtype=torch.int32, device=device)

@@ -32,11 +32,14 @@
 //    transposing LDS reads (ds_read_b64_tr_b16, two per operand). The
 //    compiler's schedule is kept: with two workgroups per CU it measured a
 //    little faster than a hand-fixed order.
-//  * Softmax in base 2 with the scale folded into one FMA before exp2. The
-//    running max used for exponentiation is only raised (and O, l rescaled)
-//    when a block's max exceeds it by more than 8 (a factor 2^8), which keeps
-//    every probability below 2^8 and skips most rescales. The row sum is
-//    taken with v_dot2 over the same bf16 probabilities that enter PV.
+//  * Softmax in base 2 with the scale folded into one FMA before exp2. A
+//    block's probabilities are formed against the running max as it stands,
+//    with no max taken first: only when some lane's share of the block's
+//    probabilities sums above 2^15 or is not finite (always the case while a
+//    row has no max yet) does the block take the row max, raise the running
+//    max, rescale O and l, and form its probabilities again. Every probability
+//    that enters PV is thus at most 2^15. The row sum is taken with v_dot2 over
+//    the same bf16 probabilities that enter PV.
 //  * Workgroups are ordered so that all query blocks of a head run on the same
 //    XCD (hardware places workgroup i on XCD i mod 8), keeping that head's
 //    prefix K/V resident in the XCD's L2.
@@ -57,7 +60,7 @@ constexpr int kWaves = 4;                 // waves per workgroup, 32 query rows 
 constexpr int kBM = 32 * kWaves;          // query rows per workgroup
 constexpr int kBN = 64;                   // keys per block
 constexpr int kTiles = kBN / 32;          // 32-key S^T tiles per block
-constexpr float kRescaleThreshold = 8.f;  // log2 units
+constexpr float kSumHi = 32768.f;  // a lane's block sum above this raises the running max
 
 typedef uint16_t Tile[kBN * kD];  // one 64-row K or V block
 
@@ -181,15 +184,22 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
   }
 
   // DMA of one 64-row K or V block: wave w fills rows 16 w .. 16 w + 15, 4
-  // instructions per wave. Element offsets fit in 32 bits (the host rejects
-  // tensors of 2^31 elements or more).
+  // instructions per wave. The tensor's base stays in scalar registers; each
+  // lane adds the byte offset of its row (clamped to the segment's last row)
+  // and of its swizzled 16-byte chunk, which is fixed for the kernel. Byte
+  // offsets fit in 32 bits (the host rejects tensors of 2^31 elements or more).
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t c16[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c16[j] = 16u * (uint32_t)((lane & 15) ^ chunk_swz(16 * wave + 4 * j + (lane >> 4)));
+  const uint32_t stride2 = 2u * stride;
   auto dma_tile = [&](const uint16_t *src, int bi, Tile &t) __attribute__((always_inline)) {
     const int kb0 = kb0_of(bi), kend = kend_of(bi);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int row0 = 16 * wave + 4 * j;
-      const int r = min(kb0 + row0 + (lane >> 4), kend - 1);
-      dma_rows(src + __umul24((uint32_t)r, stride), lane, row0, t);
+      const int row0 = 16 * wv + 4 * j;
+      const uint32_t r = (uint32_t)min(kb0 + row0 + (lane >> 4), kend - 1);
+      dma16(src, __umul24(r, stride2) + c16[j], lds_addr(reinterpret_cast<char *>(t) + row0 * kRowBytes));
     }
   };
 
@@ -208,9 +218,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
 
   // One pipeline step for block bi (P = bi & 1), its S^T computed the step
   // before: wait for K of block bi + 1 and V of block bi, start the DMA of K of
-  // block bi + 2 and V of block bi + 1, mask and take the block max, then the
-  // S^T products of block bi + 1 next to this block's exp2 /
-  // convert / row sum, then O^T += V^T P^T.
+  // block bi + 2 and V of block bi + 1, mask, then the S^T products of block
+  // bi + 1 next to this block's exp2 / convert / row sum, then O^T += V^T P^T.
   auto step = [&](int bi, auto parity, f32x16_t (&s_cur)[kTiles], f32x16_t (&s_nxt)[kTiles])
       __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;
@@ -233,21 +242,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
         xs[e] = t + (uint32_t)(32 * kt + 8 * (r >> 2) + (r & 3)) < span ? xs[e] : kNegInf;
       }
     }
-    float bmax = xs[0];
-#pragma unroll
-    for (int e = 1; e < kTiles * 16; ++e) bmax = fmaxf(bmax, xs[e]);
-    bmax = swap_halves_max(bmax);
-    // Raise the exponentiation max only when a score exceeds it by > 2^8.
-    const bool raise = bmax != kNegInf && (m == kNegInf || (bmax - m) * c > kRescaleThreshold);
-    if (__ballot(raise) != 0) {
-      const float m_new = fmaxf(m, bmax);
-      const float alpha = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);
-      l *= alpha;
-#pragma unroll
-      for (int j = 0; j < kD / 32; ++j) o[j] *= alpha;
-      m = m_new;
-    }
-    const float mc = (m == kNegInf) ? 0.f : m * c;
+    // Probabilities against the running max as it stands (m = -inf, before the
+    // row has a max, gives non-finite ones and so the rare path below).
+    const float mc = m * c;
     // S^T of block bi + 1 (a stale stage after the last block; result unused),
     // K fragments two products ahead; two probabilities per product.
     const char *kn = reinterpret_cast<const char *>(k_sm[1 - P]);
@@ -257,6 +254,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
     for (int i = 0; i < 2; ++i)
       ka[i] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(kn + koff[i % 8] + (i / 8) * 32 * kRowBytes));
     uint32_t pw[kTiles * 8];
+    float lb = 0.f;  // this lane's share of the block's probabilities
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
       const int kt = i / 8, ks = i % 8;
@@ -266,8 +264,32 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
       const float p0 = __builtin_amdgcn_exp2f(fmaf(xs[2 * i], c, -mc));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(xs[2 * i + 1], c, -mc));
       pw[i] = pack_bf16(p0, p1);
-      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[i]), kOnes, l, false);
+      lb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[i]), kOnes, lb, false);
     }
+    if (__ballot(!(lb <= kSumHi)) != 0) {
+      // Rare: raise the running max to the block's row max, rescale O and l,
+      // and form the block's probabilities again.
+      float bmax = xs[0];
+#pragma unroll
+      for (int e = 1; e < kTiles * 16; ++e) bmax = fmaxf(bmax, xs[e]);
+      bmax = swap_halves_max(bmax);
+      const float m_new = fmaxf(m, bmax);
+      const float alpha = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);
+      l *= alpha;
+#pragma unroll
+      for (int j = 0; j < kD / 32; ++j) o[j] *= alpha;
+      m = m_new;
+      const float mc2 = (m == kNegInf) ? 0.f : m * c;
+      lb = 0.f;
+#pragma unroll
+      for (int i = 0; i < kSteps; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(xs[2 * i], c, -mc2));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(xs[2 * i + 1], c, -mc2));
+        pw[i] = pack_bf16(p0, p1);
+        lb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[i]), kOnes, lb, false);
+      }
+    }
+    l += lb;
     // O^T[d][q] += V^T[d][key] P^T[key][q] over 16-key steps stp (elements
     // 8 (stp%2) .. + 7 of tile stp/2 = pw[4 stp .. 4 stp + 3]); transposing V
     // reads one product ahead.

@@ -39,8 +39,9 @@ using namespace tile;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------- pre-pass
-// D[h][i] = sum_d dO[i][h][d] O[i][h][d]; lse2[h][i] = lse[h][i] log2(e).
-// Rows past N in each head's padded stretch get D = 0, lse2 = 0.
+// nd[h][i] = -sum_d dO[i][h][d] O[i][h][d] and nlse2[h][i] = -lse[h][i] log2(e),
+// stored negated because the dK/dV products start from them. Rows past N in
+// each head's padded stretch get 0 for both.
 // 4 waves x 4 rows per block; 16 lanes per row, 16 bytes each.
 __global__ __launch_bounds__(256) void bwd_pre_kernel(MaskedBwdParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -65,8 +66,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(MaskedBwdParams p) {
   acc += __shfl_xor(acc, 4, 64);
   acc += __shfl_xor(acc, 8, 64);
   if (c == 0) {
-    p.d_row[row] = acc;
-    p.lse2[row] = i < p.seq_len ? p.lse[(int64_t)h * p.seq_len + i] * kLog2e : 0.f;
+    p.nd_row[row] = -acc;
+    p.nlse2[row] = i < p.seq_len ? -p.lse[(int64_t)h * p.seq_len + i] * kLog2e : 0.f;
   }
 }
 
@@ -141,8 +142,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(MaskedBwdParams p) {
     }
   }
   const int64_t rq = (int64_t)h * p.n_pad + row0 + (q_ok ? qi : 0);
-  const float lse2 = p.lse2[rq];
-  const float Dq = p.d_row[rq];
+  const float lse2 = -p.nlse2[rq];
+  const float Dq = -p.nd_row[rq];
   const float c = p.scale_log2;
 
   // The keys row qi sees inside each segment form one interval [lo, lo + span):
@@ -169,16 +170,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(MaskedBwdParams p) {
   }
 
   // DMA of one 32-key block: wave w fills rows 8 w .. 8 w + 7 of the K and V
-  // tiles, 4 instructions per wave and block.
+  // tiles, 4 instructions per wave and block. Tensor bases stay scalar; a lane
+  // adds the byte offset of its row (clamped to the segment's last row) and of
+  // its swizzled 16-byte chunk (fixed for the kernel).
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t stride2 = 2u * stride;
+  uint32_t c16[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) c16[j] = 16u * (uint32_t)((lane & 15) ^ chunk_swz(8 * wave + 4 * j + (lane >> 4)));
   auto dma_block = [&](int bi, DqStage &st) __attribute__((always_inline)) {
     const int kb0 = kb0_of(bi), kend = kend_of(bi);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int row0 = 8 * wave + 4 * j;
-      const int r = min(kb0 + row0 + (lane >> 4), kend - 1);
-      const uint32_t off = __umul24((uint32_t)r, stride);
-      dma_rows(Kg + off, lane, row0, st.k);
-      dma_rows(Vg + off, lane, row0, st.v);
+      const int row0 = 8 * wv + 4 * j;
+      const uint32_t r = (uint32_t)min(kb0 + row0 + (lane >> 4), kend - 1);
+      const uint32_t off = __umul24(r, stride2) + c16[j];
+      dma16(Kg, off, lds_addr(reinterpret_cast<char *>(st.k) + row0 * kRowBytes));
+      dma16(Vg, off, lds_addr(reinterpret_cast<char *>(st.v) + row0 * kRowBytes));
     }
   };
 
@@ -406,20 +414,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
     b_lo = s0;
   }
   const int nblocks = max(0, b_hi - b_lo);
-  const float *lse2_h = p.lse2 + (int64_t)h * p.n_pad + row0;
-  const float *d_h = p.d_row + (int64_t)h * p.n_pad + row0;
+  const float *lse2_h = p.nlse2 + (int64_t)h * p.n_pad + row0;
+  const float *d_h = p.nd_row + (int64_t)h * p.n_pad + row0;
 
   // DMA of one 32-row query block: wave w fills rows 4 w .. 4 w + 3 of the Q and
   // dO tiles (2 instructions) and, with its lanes 8 w .. 8 w + 7, an eighth of
   // the lse/D strip (1 instruction): 3 per wave and block.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t stride2 = 2u * stride;
+  const uint32_t c16 = 16u * (uint32_t)((lane & 15) ^ chunk_swz(4 * wave + (lane >> 4)));
   auto dma_block = [&](int bi, int stg) __attribute__((always_inline)) {
     const int qb0 = (b_lo + bi) * kBQ;
     DkdvStage &st = sm[stg];
-    const int row0 = 4 * wave;
-    const int r = min(qb0 + row0 + (lane >> 4), N - 1);
-    const uint32_t off = __umul24((uint32_t)r, stride);
-    dma_rows(Qg + off, lane, row0, st.q);
-    dma_rows(Gg + off, lane, row0, st.g);
+    const int row0 = 4 * wv;
+    const uint32_t r = (uint32_t)min(qb0 + row0 + (lane >> 4), N - 1);
+    const uint32_t off = __umul24(r, stride2) + c16;
+    dma16(Qg, off, lds_addr(reinterpret_cast<char *>(st.q) + row0 * kRowBytes));
+    dma16(Gg, off, lds_addr(reinterpret_cast<char *>(st.g) + row0 * kRowBytes));
     if ((lane >> 3) == wave) {
       // rows past the sequence's end repeat its last row, as the tile rows do
       // (their scores are masked, so P = dS = 0 whatever finite values sit here)
@@ -432,8 +443,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
 
   // Step t (t = 0 .. nblocks, both roles, one barrier each): the producers form
   // P/dS of block t (its S/dP computed in step t - 1) next to S/dP of block
-  // t + 1; the consumers run the products of block t - 1. Live stages: t - 1,
-  // t (its lse/D strip), t + 1; the other kStages - 3 hold blocks in flight
+  // t + 1; the consumers run the products of block t - 1. Live stages: t - 1
+  // (consumers) and t + 1 (Q, dO and the lse/D strip of the producers' next
+  // S/dP); stage t is not read in step t; the other kStages - 3 hold blocks in flight
   // (DMA of block t + kStages - 2 issued in step t into the stage block t - 2
   // held, whose last reader finished in step t - 1). Step t's wait: this wave's
   // part of block t + 1 landed (loads return in order: the three instructions
@@ -488,6 +500,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
         kf[ks] = as_bf16x8(k_ok ? *reinterpret_cast<const u32x4_t *>(Kg + r + ks * 16 + hi * 8) : zero);
         vf[ks] = as_bf16x8(k_ok ? *reinterpret_cast<const u32x4_t *>(Vg + r + ks * 16 + hi * 8) : zero);
       }
+      // S comes out of the products in log2 units: K scaled by c = scale log2(e)
+      // (one more bf16 rounding of K, ~2^-9 of each score, in this kernel only)
+      const float cs = p.scale_log2;
+#pragma unroll
+      for (int ks = 0; ks < kD / 16; ++ks) {
+        const u32x4_t u = __builtin_bit_cast(u32x4_t, kf[ks]);
+        u32x4_t w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = pack_bf16(__uint_as_float(u[e] << 16) * cs, __uint_as_float(u[e] & 0xffff0000u) * cs);
+        kf[ks] = as_bf16x8(w);
+      }
     }
     // Blocks that hide no (query, key) pair: all keys in the reference segment,
     // all rows output rows, block whole.
@@ -507,19 +531,36 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
     uint32_t roff[kD / 16];
 #pragma unroll
     for (int ks = 0; ks < kD / 16; ++ks) roff[ks] = row_frag_off(l32, hi, ks);
-    const float c = p.scale_log2;
 
     // S = Q K^T and dP = dO V^T of the block in stage stg: element r is query
     // qb0 + 8 (r/4) + 4 hi + r%4 of that block, key kj.
+    // The products start from -lse2 and -D of the element's row (the block's
+    // strip holds them negated), so S comes out as c s - lse2 and dP as dP - D:
+    // P = exp2(S) and dS = P dP need no further per-element term.
+    auto strip = [&](int stg, f32x16_t &nl, f32x16_t &nd) __attribute__((always_inline)) {
+      const DkdvStage &st = sm[stg];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4_t a = *reinterpret_cast<const f32x4_t *>(&st.ld[8 * g + 4 * hi]);
+        const f32x4_t b = *reinterpret_cast<const f32x4_t *>(&st.ld[kBQ + 8 * g + 4 * hi]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          nl[4 * g + e] = a[e];
+          nd[4 * g + e] = b[e];
+        }
+      }
+    };
     auto sdp = [&](int stg, f32x16_t &s, f32x16_t &dp) __attribute__((always_inline)) {
       const char *qb = reinterpret_cast<const char *>(sm[stg].q);
       const char *gb = reinterpret_cast<const char *>(sm[stg].g);
+      f32x16_t nl, nd;
+      strip(stg, nl, nd);
 #pragma unroll
       for (int ks = 0; ks < kD / 16; ++ks) {
         const bf16x8_t qa = as_bf16x8(*reinterpret_cast<const u32x4_t *>(qb + roff[ks]));
         const bf16x8_t ga = as_bf16x8(*reinterpret_cast<const u32x4_t *>(gb + roff[ks]));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], ks == 0 ? f32x16_t{} : s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], ks == 0 ? f32x16_t{} : dp, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], ks == 0 ? nl : s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], ks == 0 ? nd : dp, 0, 0, 0);
       }
     };
 
@@ -530,7 +571,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
         __attribute__((always_inline)) {
       step_sync(t, stg);
       const int qb0 = (b_lo + t) * kBQ;
-      const DkdvStage &st = sm[stg];
       float xs[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) xs[r] = s_cur[r];
@@ -541,15 +581,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
           xs[r] = tt + (uint32_t)(8 * (r >> 2) + (r & 3)) < v_span ? xs[r] : kNegInf;
       }
       __builtin_amdgcn_sched_barrier(0);
-      // lse/D of this block's rows 8 g + 4 hi .. + 3 (broadcast reads).
-      f32x4_t l4[4], d4[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        l4[g] = *reinterpret_cast<const f32x4_t *>(&st.ld[8 * g + 4 * hi]);
-        d4[g] = *reinterpret_cast<const f32x4_t *>(&st.ld[kBQ + 8 * g + 4 * hi]);
-      }
       // S/dP of block t + 1 (a stale stage after the last block; result unused).
       const int nstg = ring(stg, 1);
+      f32x16_t nl, nd;
+      strip(nstg, nl, nd);
       const char *qn = reinterpret_cast<const char *>(sm[nstg].q);
       const char *gn = reinterpret_cast<const char *>(sm[nstg].g);
       bf16x8_t qa[kD / 16], ga[kD / 16];
@@ -565,14 +600,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
           qa[ks + 2] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(qn + roff[ks + 2]));
           ga[ks + 2] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(gn + roff[ks + 2]));
         }
-        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], ks == 0 ? f32x16_t{} : s_nxt, 0, 0, 0);
-        dp_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[ks], vf[ks], ks == 0 ? f32x16_t{} : dp_nxt, 0, 0, 0);
+        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], ks == 0 ? nl : s_nxt, 0, 0, 0);
+        dp_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[ks], vf[ks], ks == 0 ? nd : dp_nxt, 0, 0, 0);
         // elements 2 ks, 2 ks + 1: rows 8 (ks/2) + 4 hi + 2 (ks%2) + {0, 1}
-        const int g = ks >> 1, e = 2 * (ks & 1);
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(xs[2 * ks], c, -l4[g][e]));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(xs[2 * ks + 1], c, -l4[g][e + 1]));
+        const float p0 = __builtin_amdgcn_exp2f(xs[2 * ks]);
+        const float p1 = __builtin_amdgcn_exp2f(xs[2 * ks + 1]);
         pw[ks] = pack_bf16(p0, p1);
-        dw[ks] = pack_bf16(p0 * (dp_cur[2 * ks] - d4[g][e]), p1 * (dp_cur[2 * ks + 1] - d4[g][e + 1]));
+        dw[ks] = pack_bf16(p0 * dp_cur[2 * ks], p1 * dp_cur[2 * ks + 1]);
         // Step st2 of the consumer's products uses elements 8 st2 .. 8 st2 + 7;
         // storing each half as soon as it exists keeps the arithmetic between
         // the products.

@@ -76,17 +76,27 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void_t *)p));
 }
 
-// M0 is saved and restored around the instruction: the compiler reserves it.
-__device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
+// 16 bytes per lane from a wave-uniform 64-bit base in scalar registers plus a
+// 32-bit per-lane byte offset (the instruction's saddr form). M0 is saved and
+// restored around the instruction: the compiler reserves it.
+__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds_base) {
+  // The base is the same in every lane; say so where the compiler cannot tell.
+  const uint64_t a = reinterpret_cast<uintptr_t>(sbase);
+  // (readfirstlane returns int: each half goes through uint32_t, never sign-extended)
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint64_t ua = (uint64_t)lo | ((uint64_t)hi << 32);
+  sbase = reinterpret_cast<const void *>(ua);
   uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
       : "memory");
 }
 
+// 4 bytes per lane from a per-lane 64-bit address.
 __device__ __forceinline__ void dma4(const void *src, uint32_t lds_base) {
   uint32_t saved;
   asm volatile(
@@ -110,16 +120,6 @@ template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(n >= 0 && n < 16, "vmcnt field");
   __builtin_amdgcn_s_waitcnt(0x0f70 | n);
-}
-
-// One DMA instruction (global_load_lds_dwordx4): 64 lanes x 16 bytes land at
-// tile + row0 * 256 + 16 lane, i.e. rows row0 .. row0 + 3, physical chunk
-// lane % 16. Lane L loads global row `src_row` (already clamped by the caller),
-// logical chunk (L % 16) ^ chunk_swz(row0 + L / 16).
-__device__ __forceinline__ void dma_rows(const uint16_t *src_row, int lane, int row0, uint16_t *tile) {
-  const int r = row0 + (lane >> 4);
-  const int c = (lane & 15) ^ chunk_swz(r);
-  dma16(src_row + 8 * c, lds_addr(reinterpret_cast<char *>(tile) + row0 * kRowBytes));
 }
 
 }  // namespace tile
