@@ -430,9 +430,10 @@ def main():
         del rc, rq, rk, rv, rout, rws
 
         progress("ragged batch measured")
-        gemm = gemm_tflops(torch, stream)
-        mfma_rate = mfma_probe_tflops(torch, rs, stream)
-        # packed 32K masked forward (matrix cores)
+        # packed 32K masked forward (matrix cores); each figure is the median of three
+        # timed runs, taken before the GEMM and matrix-core probes below so that
+        # their heat does not lower the clock the packed kernels are timed at
+        med3 = lambda f, iters: sorted(event_time_ms(f, iters, stream) / iters for _ in range(3))[1]
         mw = wl.PACKED_32K
         Q, Kp, Vp = wl.packed_qkv(mw)
         to_d = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
@@ -444,13 +445,11 @@ def main():
                                                 mw.head_dim, rs.RSWA_BF16, mode, 0.0, stream=stream)
             for _ in range(5):
                 run(0)
-            ms_m = event_time_ms(run, 20, stream) / 20
+            ms_m = med3(run, 20)
             fl = masked_flops(mw.seq_len, mw.ref_len, mw.window, mw.heads, mw.head_dim,
                               mode == rs.RSWA_PREFIX_FULL)
             masked[name] = {"ms": ms_m, "algorithmic_flop": fl, "TFLOPs": fl / (ms_m * 1e-3) / 1e12,
-                            "frac_of_bf16_peak": fl / (ms_m * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                            "frac_of_measured_gemm": fl / (ms_m * 1e-3) / 1e12 / gemm,
-                            "frac_of_measured_mfma_rate": fl / (ms_m * 1e-3) / 1e12 / mfma_rate}
+                            "frac_of_bf16_peak": fl / (ms_m * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
         # packed 32K backward (dQ, dK, dV) of the causal-prefix forward
         Gd = to_d(wl.packed_dout(mw))
         lse = torch.empty((mw.heads, mw.seq_len), dtype=torch.float32, device="cuda")
@@ -464,23 +463,18 @@ def main():
                                                   rs.RSWA_PREFIX_CAUSAL, 0.0, ws_b, stream=stream)
         for _ in range(3):
             run_b(0)
-        ms_b = event_time_ms(run_b, 10, stream) / 10
+        ms_b = med3(run_b, 5)
         fl_b = 2.5 * masked_flops(mw.seq_len, mw.ref_len, mw.window, mw.heads, mw.head_dim, False)
         masked["backward_prefix_causal"] = {
             "ms": ms_b, "algorithmic_flop": fl_b, "TFLOPs": fl_b / (ms_b * 1e-3) / 1e12,
             "frac_of_bf16_peak": fl_b / (ms_b * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            "frac_of_measured_mfma_rate": fl_b / (ms_b * 1e-3) / 1e12 / mfma_rate,
             "flop_convention": "2.5x the forward: five products of 2 d flop per visible pair (S, dP, dV, dK, "
                                "dQ); the kernels execute seven (S and dP are formed in both the dQ and "
                                "the dK/dV pass)",
             "calls": "lse-producing forward excluded; pre-pass, dQ, dK/dV and reduction kernels included"}
         del ws_b
         result["masked_32k"] = {"workload": mw.name, "seq_len": mw.seq_len, "ref_len": mw.ref_len,
-                                "window": mw.window, "heads": mw.heads,
-                                "measured_bf16_gemm_TFLOPs": gemm, "gemm": "8192^3 bf16 torch.matmul",
-                                "measured_mfma_rate_TFLOPs": mfma_rate,
-                                "mfma_rate": "rswa_probe_mfma: 32x32x16 bf16 products back to back, two waves "
-                                             "per SIMD, nothing else in the loop", **masked}
+                                "window": mw.window, "heads": mw.heads, **masked}
         if not args.no_cpu_baseline:
             result["cpu_baseline_masked"] = cpu_masked_rows(mw, Q, Kp, Vp)
 
@@ -495,7 +489,7 @@ def main():
                                                      rs.RSWA_BF16, rs.RSWA_PREFIX_CAUSAL, 0.0, stream=stream)
         for _ in range(5):
             run_v(0)
-        ms_v = event_time_ms(run_v, 20, stream) / 20
+        ms_v = med3(run_v, 20)
         fl_v = sum(masked_flops(int(N_s), int(L_s), mw.window, mw.heads, mw.head_dim, False)
                    for N_s, L_s in zip(lens, refs))
         # backward of the same pack (dO as for the single-sequence backward)
@@ -510,7 +504,7 @@ def main():
                                                           rs.RSWA_PREFIX_CAUSAL, 0.0, ws_v, stream=stream)
         for _ in range(3):
             run_vb(0)
-        ms_vb = event_time_ms(run_vb, 10, stream) / 10
+        ms_vb = med3(run_vb, 5)
         result["varlen_32k"] = {
             "workload": "packed-32k-varlen-bf16", "samples": len(refs),
             "sample_rows": [int(x) for x in lens], "ref_lens": [int(x) for x in refs],
@@ -560,6 +554,19 @@ def main():
             "note": "one launch: the packed forward with the cache write fused into each workgroup's tail; "
                     "forward_only_ms is the same pack through rswa_masked_attn_varlen"}
         del pq, pk, pv, pout, pcache
+        # chip reference rates, measured after every packed kernel was timed
+        gemm = gemm_tflops(torch, stream)
+        mfma_rate = mfma_probe_tflops(torch, rs, stream)
+        mk = result["masked_32k"]
+        mk.update({"measured_bf16_gemm_TFLOPs": gemm, "gemm": "8192^3 bf16 torch.matmul",
+                   "measured_mfma_rate_TFLOPs": mfma_rate,
+                   "mfma_rate": "rswa_probe_mfma: 32x32x16 bf16 products back to back, two waves "
+                                "per SIMD, nothing else in the loop; both probes run after the packed "
+                                "kernels were timed"})
+        for name in ("prefix_causal", "prefix_full", "backward_prefix_causal"):
+            if name != "backward_prefix_causal":
+                mk[name]["frac_of_measured_gemm"] = mk[name]["TFLOPs"] / gemm
+            mk[name]["frac_of_measured_mfma_rate"] = mk[name]["TFLOPs"] / mfma_rate
 
         progress("prefill measured")
         # a decode step through `layers` attention layers (own cache each) as one HIP graph, at the
