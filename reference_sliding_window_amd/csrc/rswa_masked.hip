@@ -193,13 +193,25 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
 #pragma unroll
   for (int j = 0; j < 4; ++j) c16[j] = 16u * (uint32_t)((lane & 15) ^ chunk_swz(16 * wave + 4 * j + (lane >> 4)));
   const uint32_t stride2 = 2u * stride;
-  auto dma_tile = [&](const uint16_t *src, int bi, Tile &t) __attribute__((always_inline)) {
-    const int kb0 = kb0_of(bi), kend = kend_of(bi);
+  const uint32_t k_lds[2] = {lds_addr(&k_sm[0][0]), lds_addr(&k_sm[1][0])};
+  const uint32_t v_lds[2] = {lds_addr(&v_sm[0][0]), lds_addr(&v_sm[1][0])};
+  uint32_t c16r[4];  // instruction j: its chunk offset plus its 4 j rows
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row0 = 16 * wv + 4 * j;
-      const uint32_t r = (uint32_t)min(kb0 + row0 + (lane >> 4), kend - 1);
-      dma16(src, __umul24(r, stride2) + c16[j], lds_addr(reinterpret_cast<char *>(t) + row0 * kRowBytes));
+  for (int j = 0; j < 4; ++j) c16r[j] = c16[j] + 4u * (uint32_t)j * stride2;
+  auto dma_tile = [&](const uint16_t *src, int bi, uint32_t t_lds) __attribute__((always_inline)) {
+    const int kb0 = kb0_of(bi), kend = kend_of(bi);
+    if (kb0 + kBN <= kend) {  // a whole block: one row product per lane
+      const uint32_t rb = __umul24((uint32_t)(kb0 + 16 * wv + (lane >> 4)), stride2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dma16(src, rb + c16r[j], t_lds + (uint32_t)((16 * wv + 4 * j) * kRowBytes));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row0 = 16 * wv + 4 * j;
+        const uint32_t r = (uint32_t)min(kb0 + row0 + (lane >> 4), kend - 1);
+        dma16(src, __umul24(r, stride2) + c16[j], t_lds + (uint32_t)(row0 * kRowBytes));
+      }
     }
   };
 
@@ -225,8 +237,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
     constexpr int P = decltype(parity)::value;
     wait_vmcnt<0>();  // everything issued one step ago landed
     block_barrier();  // for every wave; K stage P and V stage 1 - P are free
-    if (bi + 2 < nblocks) dma_tile(Kg, bi + 2, k_sm[P]);
-    if (bi + 1 < nblocks) dma_tile(Vg, bi + 1, v_sm[1 - P]);
+    if (bi + 2 < nblocks) dma_tile(Kg, bi + 2, k_lds[P]);
+    if (bi + 1 < nblocks) dma_tile(Vg, bi + 1, v_lds[1 - P]);
     float xs[kTiles * 16];
 #pragma unroll
     for (int kt = 0; kt < kTiles; ++kt)
@@ -309,9 +321,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
   wait_vmcnt<0>();  // resident Q rows landed (the compiler does not count the DMA)
   f32x16_t sa[kTiles] = {}, sb[kTiles] = {};
   if (nblocks > 0) {
-    dma_tile(Kg, 0, k_sm[0]);
-    dma_tile(Vg, 0, v_sm[0]);
-    if (nblocks > 1) dma_tile(Kg, 1, k_sm[1]);
+    dma_tile(Kg, 0, k_lds[0]);
+    dma_tile(Vg, 0, v_lds[0]);
+    if (nblocks > 1) dma_tile(Kg, 1, k_lds[1]);
     wait_vmcnt<0>();
     block_barrier();
     qk(k_sm[0], sa);

@@ -178,15 +178,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(MaskedBwdParams p) {
   uint32_t c16[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) c16[j] = 16u * (uint32_t)((lane & 15) ^ chunk_swz(8 * wave + 4 * j + (lane >> 4)));
-  auto dma_block = [&](int bi, DqStage &st) __attribute__((always_inline)) {
+  const uint32_t sm_lds = lds_addr(&sm[0]);
+  const uint32_t c16r1 = c16[1] + 4u * stride2;  // instruction 1: four rows further
+  auto dma_block = [&](int bi, int stg) __attribute__((always_inline)) {
     const int kb0 = kb0_of(bi), kend = kend_of(bi);
+    const uint32_t k_lds = sm_lds + (uint32_t)(stg * sizeof(DqStage) + offsetof(DqStage, k));
+    const uint32_t v_lds = sm_lds + (uint32_t)(stg * sizeof(DqStage) + offsetof(DqStage, v));
+    uint32_t off[2];
+    if (kb0 + kBNq <= kend) {  // a whole block: one row product per lane
+      const uint32_t rb = __umul24((uint32_t)(kb0 + 8 * wv + (lane >> 4)), stride2);
+      off[0] = rb + c16[0];
+      off[1] = rb + c16r1;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t r = (uint32_t)min(kb0 + 8 * wv + 4 * j + (lane >> 4), kend - 1);
+        off[j] = __umul24(r, stride2) + c16[j];
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int row0 = 8 * wv + 4 * j;
-      const uint32_t r = (uint32_t)min(kb0 + row0 + (lane >> 4), kend - 1);
-      const uint32_t off = __umul24(r, stride2) + c16[j];
-      dma16(Kg, off, lds_addr(reinterpret_cast<char *>(st.k) + row0 * kRowBytes));
-      dma16(Vg, off, lds_addr(reinterpret_cast<char *>(st.v) + row0 * kRowBytes));
+      const uint32_t row_lds = (uint32_t)((8 * wv + 4 * j) * kRowBytes);
+      dma16(Kg, off[j], k_lds + row_lds);
+      dma16(Vg, off[j], v_lds + row_lds);
     }
   };
 
@@ -216,7 +230,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(MaskedBwdParams p) {
     else
       wait_vmcnt<0>();
     block_barrier();  // every wave's part of block bi + 1 landed; stage (bi + 3) & 3 is free
-    if (bi + 3 < nblocks) dma_block(bi + 3, sm[(bi + 3) & 3]);
+    if (bi + 3 < nblocks) dma_block(bi + 3, (bi + 3) & 3);
     float xs[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) xs[r] = s_cur[r];
@@ -269,7 +283,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(MaskedBwdParams p) {
   wait_vmcnt<0>();  // resident Q/dO rows landed (the compiler does not count the DMA)
 #pragma unroll
   for (int j = 0; j < 3; ++j)
-    if (j < nblocks) dma_block(j, sm[j]);
+    if (j < nblocks) dma_block(j, j);
   f32x16_t sa = {}, dpa = {}, sb = {}, dpb = {};
   if (nblocks > 0) {
     // block 0 landed: blocks 1 and 2 (four instructions each) may be outstanding
@@ -423,20 +437,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t stride2 = 2u * stride;
   const uint32_t c16 = 16u * (uint32_t)((lane & 15) ^ chunk_swz(4 * wave + (lane >> 4)));
+  const uint32_t sm_lds = lds_addr(&sm[0]);
   auto dma_block = [&](int bi, int stg) __attribute__((always_inline)) {
     const int qb0 = (b_lo + bi) * kBQ;
-    DkdvStage &st = sm[stg];
+    const uint32_t st_lds = sm_lds + (uint32_t)(stg * sizeof(DkdvStage));
     const int row0 = 4 * wv;
     const uint32_t r = (uint32_t)min(qb0 + row0 + (lane >> 4), N - 1);
     const uint32_t off = __umul24(r, stride2) + c16;
-    dma16(Qg, off, lds_addr(reinterpret_cast<char *>(st.q) + row0 * kRowBytes));
-    dma16(Gg, off, lds_addr(reinterpret_cast<char *>(st.g) + row0 * kRowBytes));
+    dma16(Qg, off, st_lds + (uint32_t)(offsetof(DkdvStage, q) + row0 * kRowBytes));
+    dma16(Gg, off, st_lds + (uint32_t)(offsetof(DkdvStage, g) + row0 * kRowBytes));
     if ((lane >> 3) == wave) {
       // rows past the sequence's end repeat its last row, as the tile rows do
       // (their scores are masked, so P = dS = 0 whatever finite values sit here)
       const int rr = min(qb0 + (lane & 31), N - 1);
       const float *src = lane < 32 ? lse2_h + rr : d_h + rr;
-      dma4(src, lds_addr(st.ld));  // lane L's dword lands at st.ld[L]
+      dma4(src, st_lds + (uint32_t)offsetof(DkdvStage, ld));  // lane L's dword lands at ld[L]
     }
   };
   auto ring = [](int s, int k) __attribute__((always_inline)) { return s + k < kStages ? s + k : s + k - kStages; };
