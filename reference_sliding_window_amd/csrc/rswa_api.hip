@@ -508,13 +508,13 @@ rswa_status_t rswa_masked_attn_bwd(const void *q, const void *k, const void *v, 
   p.seq_len = seq_len;
   p.n_pad = plan.n_pad;
   p.nd_row = static_cast<float *>(workspace);
-  p.nlse2 = p.nd_row + (size_t)num_heads * p.n_pad;
+  p.nls = p.nd_row + (size_t)num_heads * p.n_pad;
   p.parts = plan.parts;
   p.nkb_pre = plan.nkb_pre;
   p.nkb_win = plan.nkb_win;
   p.kpre = plan.kpre;
   if (plan.parts > 1) {
-    p.part_dk = p.nlse2 + (size_t)num_heads * p.n_pad;
+    p.part_dk = p.nls + (size_t)num_heads * p.n_pad;
     p.part_dv = p.part_dk + (size_t)plan.parts * num_heads * plan.kpre * 128;
   }
   p.ref_len = ref_len;
@@ -579,7 +579,7 @@ rswa_status_t rswa_masked_attn_bwd_varlen(const void *q, const void *k, const vo
   p.seq_len = total_tokens;
   p.n_pad = (int32_t)(need / (2 * (size_t)num_heads * sizeof(float)));
   p.nd_row = static_cast<float *>(workspace);
-  p.nlse2 = p.nd_row + (size_t)num_heads * p.n_pad;
+  p.nls = p.nd_row + (size_t)num_heads * p.n_pad;
   p.parts = 1;
   p.cu_seqlens = cu_seqlens;
   p.ref_lens = ref_lens;

@@ -124,7 +124,7 @@ struct MaskedBwdParams {
   void *dk;
   void *dv;
   float *nd_row;   // workspace [H][n_pad]: -(dO_i . O_i)
-  float *nlse2;    // workspace [H][n_pad]: -lse_i in base 2
+  float *nls;      // workspace [H][n_pad]: -lse_i / scale (raw score units)
   float *part_dk;  // workspace [parts][H][kpre][d]: partial dK of the segment's key blocks
   float *part_dv;  // workspace [parts][H][kpre][d]
   int32_t seq_len, n_pad, ref_len, window, heads, prefix_mode;
@@ -152,7 +152,7 @@ hipError_t launch_masked(const MaskedParams &p, int32_t head_dim, hipStream_t s)
 // Work split of the packed backward (host-known sizes only).
 struct BwdPlan {
   int32_t parts, nkb_pre, nkb_win, n_pad, kpre;
-  size_t bytes_rows;   // nd_row + nlse2
+  size_t bytes_rows;   // nd_row + nls
   size_t bytes_parts;  // part_dk + part_dv (0 when parts == 1)
 };
 BwdPlan plan_masked_bwd(int32_t seq_len, int32_t ref_len, int32_t heads, int32_t requested_parts);

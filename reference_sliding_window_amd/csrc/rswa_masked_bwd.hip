@@ -36,12 +36,11 @@ namespace {
 
 using namespace tile;
 
-constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------- pre-pass
-// nd[h][i] = -sum_d dO[i][h][d] O[i][h][d] and nlse2[h][i] = -lse[h][i] log2(e),
-// stored negated because the dK/dV products start from them. Rows past N in
-// each head's padded stretch get 0 for both.
+// nd[h][i] = -sum_d dO[i][h][d] O[i][h][d] and nls[h][i] = -lse[h][i] / scale (in
+// the units of the unscaled scores), stored so because the dK/dV products start
+// from them. Rows past N in each head's padded stretch get 0 for both.
 // 4 waves x 4 rows per block; 16 lanes per row, 16 bytes each.
 __global__ __launch_bounds__(256) void bwd_pre_kernel(MaskedBwdParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -67,7 +66,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(MaskedBwdParams p) {
   acc += __shfl_xor(acc, 8, 64);
   if (c == 0) {
     p.nd_row[row] = -acc;
-    p.nlse2[row] = i < p.seq_len ? -p.lse[(int64_t)h * p.seq_len + i] * kLog2e : 0.f;
+    p.nls[row] = i < p.seq_len ? -p.lse[(int64_t)h * p.seq_len + i] / p.scale : 0.f;
   }
 }
 
@@ -142,9 +141,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(MaskedBwdParams p) {
     }
   }
   const int64_t rq = (int64_t)h * p.n_pad + row0 + (q_ok ? qi : 0);
-  const float lse2 = -p.nlse2[rq];
   const float Dq = -p.nd_row[rq];
   const float c = p.scale_log2;
+  const float nlc = p.nls[rq] * c;  // -lse in base 2
 
   // The keys row qi sees inside each segment form one interval [lo, lo + span):
   // the reference segment up to L_m (or up to the row itself for a causal row
@@ -260,8 +259,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(MaskedBwdParams p) {
       }
       s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], ks == 0 ? f32x16_t{} : s_nxt, 0, 0, 0);
       dp_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], gf[ks], ks == 0 ? f32x16_t{} : dp_nxt, 0, 0, 0);
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(xs[2 * ks], c, -lse2));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(xs[2 * ks + 1], c, -lse2));
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(xs[2 * ks], c, nlc));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(xs[2 * ks + 1], c, nlc));
       dw[ks] = pack_bf16(p0 * (dp_cur[2 * ks] - Dq), p1 * (dp_cur[2 * ks + 1] - Dq));
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -428,7 +427,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
     b_lo = s0;
   }
   const int nblocks = max(0, b_hi - b_lo);
-  const float *lse2_h = p.nlse2 + (int64_t)h * p.n_pad + row0;
+  const float *lse2_h = p.nls + (int64_t)h * p.n_pad + row0;
   const float *d_h = p.nd_row + (int64_t)h * p.n_pad + row0;
 
   // DMA of one 32-row query block: wave w fills rows 4 w .. 4 w + 3 of the Q and
@@ -515,18 +514,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
         kf[ks] = as_bf16x8(k_ok ? *reinterpret_cast<const u32x4_t *>(Kg + r + ks * 16 + hi * 8) : zero);
         vf[ks] = as_bf16x8(k_ok ? *reinterpret_cast<const u32x4_t *>(Vg + r + ks * 16 + hi * 8) : zero);
       }
-      // S comes out of the products in log2 units: K scaled by c = scale log2(e)
-      // (one more bf16 rounding of K, ~2^-9 of each score, in this kernel only)
-      const float cs = p.scale_log2;
-#pragma unroll
-      for (int ks = 0; ks < kD / 16; ++ks) {
-        const u32x4_t u = __builtin_bit_cast(u32x4_t, kf[ks]);
-        u32x4_t w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = pack_bf16(__uint_as_float(u[e] << 16) * cs, __uint_as_float(u[e] & 0xffff0000u) * cs);
-        kf[ks] = as_bf16x8(w);
-      }
     }
     // Blocks that hide no (query, key) pair: all keys in the reference segment,
     // all rows output rows, block whole.
@@ -546,12 +533,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
     uint32_t roff[kD / 16];
 #pragma unroll
     for (int ks = 0; ks < kD / 16; ++ks) roff[ks] = row_frag_off(l32, hi, ks);
+    const float c = p.scale_log2;
 
     // S = Q K^T and dP = dO V^T of the block in stage stg: element r is query
     // qb0 + 8 (r/4) + 4 hi + r%4 of that block, key kj.
-    // The products start from -lse2 and -D of the element's row (the block's
-    // strip holds them negated), so S comes out as c s - lse2 and dP as dP - D:
-    // P = exp2(S) and dS = P dP need no further per-element term.
+    // The products start from -lse/scale and -D of the element's row (the
+    // block's strip holds them so), so S comes out as s - lse/scale and dP as
+    // dP - D: P = exp2(c S) and dS = P dP need no subtraction per element.
     auto strip = [&](int stg, f32x16_t &nl, f32x16_t &nd) __attribute__((always_inline)) {
       const DkdvStage &st = sm[stg];
 #pragma unroll
@@ -618,8 +606,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
         s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], ks == 0 ? nl : s_nxt, 0, 0, 0);
         dp_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[ks], vf[ks], ks == 0 ? nd : dp_nxt, 0, 0, 0);
         // elements 2 ks, 2 ks + 1: rows 8 (ks/2) + 4 hi + 2 (ks%2) + {0, 1}
-        const float p0 = __builtin_amdgcn_exp2f(xs[2 * ks]);
-        const float p1 = __builtin_amdgcn_exp2f(xs[2 * ks + 1]);
+        const float p0 = __builtin_amdgcn_exp2f(xs[2 * ks] * c);
+        const float p1 = __builtin_amdgcn_exp2f(xs[2 * ks + 1] * c);
         pw[ks] = pack_bf16(p0, p1);
         dw[ks] = pack_bf16(p0 * dp_cur[2 * ks], p1 * dp_cur[2 * ks + 1]);
         // Step st2 of the consumer's products uses elements 8 st2 .. 8 st2 + 7;

@@ -102,6 +102,26 @@ def check_grad(got: np.ndarray, ref: np.ndarray, what: str):
     return maxabs, hrel
 
 
+def score_range_qkv(N: int, H: int = 4, d: int = 128, seed: int = 20261204):
+    """Packed Q, K, V ([N][H][d], bf16 storage bits) whose scores leave the unit range,
+    per head: head 0 grows along the sequence (key j scaled by 1 + j/60, queries by 2:
+    about -105 .. 107 at N = 700, d = 128, so later blocks keep exceeding the running
+    max), head 1 is strongly negative (q = -5u, k = u, plus unit noise: about -84 .. -46),
+    head 2 strongly positive (q = 8u: about 68 .. 131), head 3 ordinary N(0, 1). The
+    construction only scales and mixes seeded Gaussian draws."""
+    g = lambda i, shape: wl.to_f64(wl.draw("bf16", 1.0, shape, seed, i), "bf16")
+    Q, K, V = g(0, (N, H, d)), g(1, (N, H, d)), g(2, (N, H, d))
+    u = g(3, (d,))
+    j = np.arange(N, dtype=np.float64)[:, None]
+    K[:, 0] *= 1.0 + j / 60.0
+    Q[:, 0] *= 2.0
+    K[:, 1] = u + K[:, 1]
+    Q[:, 1] = -5.0 * u + Q[:, 1]
+    K[:, 2] = u + K[:, 2]
+    Q[:, 2] = 8.0 * u + Q[:, 2]
+    return tuple(wl.f32_to_bf16_bits(x.astype(np.float32)) for x in (Q, K, V))
+
+
 class DecodeRun:
     """Drives a batch-synchronous decode workload through the C ABI."""
 

@@ -20,7 +20,7 @@ import oracle.pool as opool
 import oracle.rswa as orc
 import reference_sliding_window_amd as rs
 import workloads as wl
-from gpu_util import check_close, check_grad, to_dev, to_f64
+from gpu_util import check_close, check_grad, score_range_qkv, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -299,3 +299,27 @@ class _RowView:
         if isinstance(i, tuple):
             return self.a[self.pos[int(i[0])]][i[1:]]
         return self.a[self.pos[int(i)]]
+
+
+@pytest.mark.parametrize("mode", [CAUSAL, FULL])
+def test_backward_score_ranges(mode):
+    """Gradients where the scores leave the unit range (score_range_qkv: a head whose
+    scores grow to about +-100 along the sequence, one strongly negative, one strongly
+    positive, one ordinary): dQ, dK, dV of every row and key against the oracle."""
+    N, L_m, n, H = 700, 200, 64, 4
+    banner(f"backward score ranges mode={mode}")
+    r = PackedRun(N, L_m, n, H, mode, seed=77001)
+    r.Q, r.K, r.V = score_range_qkv(N, H)
+    r.Qd, r.Kd, r.Vd = (to_dev(x, "bf16") for x in (r.Q, r.K, r.V))
+    r.forward()
+    r.backward()
+    torch.cuda.synchronize()
+    Qf, Kf, Vf, Gf = r.f64()
+    scale = 1.0 / np.sqrt(128)
+    ref_o = orc.masked_attention_rows(Qf, Kf, Vf, range(N), L_m, n, scale, mode)
+    check_close(to_f64(r.out), ref_o, "bf16", f"forward score ranges mode={mode}")
+    dQ, dK, dV = orc.masked_attention_backward(Qf, Kf, Vf, Gf, L_m, n, scale, mode)
+    tag = f"score ranges mode={mode}"
+    check_grad(to_f64(r.dq), dQ, f"dQ {tag}")
+    check_grad(to_f64(r.dk), dK, f"dK {tag}")
+    check_grad(to_f64(r.dv), dV, f"dV {tag}")

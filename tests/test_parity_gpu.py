@@ -16,8 +16,8 @@ import oracle.rswa as orc
 import reference_sliding_window_amd as rs
 import workloads as wl
 import oracle.pool as opool
-from gpu_util import (DecodeRun, bits, check_close, oracle_decode_all_pairs, shared_decode_inputs,
-                      storage_bits, to_dev, to_f64)
+from gpu_util import (DecodeRun, bits, check_close, oracle_decode_all_pairs, score_range_qkv,
+                      shared_decode_inputs, storage_bits, to_dev, to_f64)
 
 DTYPE = {"bf16": rs.RSWA_BF16, "fp32": rs.RSWA_FP32}
 
@@ -525,6 +525,32 @@ def test_masked_small_every_row(N, L_m, n, mode):
     f = lambda a: wl.to_f64(a, "bf16")
     ref = orc.masked_attention_rows(f(Q), f(K), f(V), range(N), L_m, n, mw.scale, mode)
     check_close(got, ref, "bf16", f"packed N={N} L_m={L_m} n={n} mode={mode}")
+
+
+@pytest.mark.parametrize("mode", [rs.RSWA_PREFIX_CAUSAL, rs.RSWA_PREFIX_FULL])
+def test_masked_score_ranges(mode):
+    """Scores far from the unit range (score_range_qkv: growing along the sequence, so
+    later blocks keep exceeding the running max many times over; strongly negative;
+    strongly positive; ordinary). The kernel forms a block's
+    probabilities against the running max before looking at the block, so these rows
+    exercise its raise-and-retake path; every row against the oracle (Eqs. (3)-(4) of
+    the pages' attention do not depend on the max used)."""
+    N, L_m, n, H = 700, 200, 64, 4
+    banner(f"packed score ranges mode={mode}")
+    Qb, Kb, Vb = score_range_qkv(N, H)
+    Qf, Kf, Vf = (wl.to_f64(x, "bf16") for x in (Qb, Kb, Vb))
+    scale = 1.0 / math.sqrt(128)
+    s1 = np.einsum("id,id->i", Qf[:, 1], Kf[:, 1]) * scale
+    s2 = np.einsum("id,id->i", Qf[:, 2], Kf[:, 2]) * scale
+    assert s1.max() < -30 and s2.min() > 30        # the ranges the heads are built for
+    out = torch.empty((N, H, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((H, N), dtype=torch.float32, device="cuda")
+    rs.rswa_masked_attn(to_dev(Qb, "bf16"), to_dev(Kb, "bf16"), to_dev(Vb, "bf16"), out, N, L_m, n, H, 128,
+                        rs.RSWA_BF16, mode, 0.0, lse=lse)
+    torch.cuda.synchronize()
+    ref = orc.masked_attention_rows(Qf, Kf, Vf, range(N), L_m, n, scale, mode)
+    check_close(to_f64(out), ref, "bf16", f"score ranges mode={mode}")
+    assert np.isfinite(lse.cpu().numpy()).all()
 
 
 def test_masked_rows_agree_with_decode_kernel():
