@@ -154,6 +154,32 @@ def mfma_probe_tflops(torch, rs, stream, iters=4096, workgroups=512):
     return workgroups * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12
 
 
+def cu_probe(torch, rs, stream, workgroups=256):
+    """Per-CU rates of the other units the packed kernels lean on, in shader-clock cycles
+    (rswa_probe_cu: one workgroup of 8 waves per CU, cycles counted on the device)."""
+    out = torch.zeros(2 * workgroups, dtype=torch.int32, device="cuda")
+    res = {}
+    for kind, name, iters in ((rs.RSWA_PROBE_LDS_B128, "lds_ds_read_b128", 512),
+                              (rs.RSWA_PROBE_LDS_TR16, "lds_ds_read_b64_tr_b16", 512),
+                              (rs.RSWA_PROBE_EXP, "v_exp_f32", 8192), (rs.RSWA_PROBE_FMA, "v_fma_f32", 8192)):
+        run = lambda i: rs.rswa_probe_cu(out, workgroups, iters, kind, stream=stream)
+        for _ in range(3):
+            run(0)
+        ms = event_time_ms(run, 5, stream) / 5
+        cycles = float(np.median(out.view(torch.int32).cpu().numpy()[0::2].astype(np.uint32)))
+        if kind in (rs.RSWA_PROBE_LDS_B128, rs.RSWA_PROBE_LDS_TR16):
+            res[name + "_bytes_per_clk_per_cu"] = 8 * iters * 16384 / cycles
+        else:
+            res[name + "_cycles_per_wave_instruction_per_simd"] = cycles / (2 * iters * 8)
+        res[name + "_shader_clock_GHz"] = cycles / (ms * 1e-3) / 1e9
+    res["how"] = ("rswa_probe_cu: 256 workgroups of 8 waves (one per CU, two waves per SIMD); LDS kinds: 16 KB "
+                  "per wave per round, "
+                  "the forward's K-fragment (ds_read_b128) and V^T (ds_read_b64_tr_b16) patterns on its "
+                  "swizzled tiles; exp/fma: 8 independent instructions per wave per round; median cycles "
+                  "over workgroups (s_memtime); the clock is those cycles over the kernel's event time")
+    return res
+
+
 def gemm_tflops(torch, stream, m=8192):
     """A large bf16 GEMM through the vendor library: the measured matrix-core reference."""
     a = torch.randn((m, m), device="cuda").to(torch.bfloat16)
@@ -557,6 +583,7 @@ def main():
         # chip reference rates, measured after every packed kernel was timed
         gemm = gemm_tflops(torch, stream)
         mfma_rate = mfma_probe_tflops(torch, rs, stream)
+        result["cu_probe"] = cu_probe(torch, rs, stream)
         mk = result["masked_32k"]
         mk.update({"measured_bf16_gemm_TFLOPs": gemm, "gemm": "8192^3 bf16 torch.matmul",
                    "measured_mfma_rate_TFLOPs": mfma_rate,

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define RSWA_ABI_VERSION 7
+#define RSWA_ABI_VERSION 8
 
 #if defined(__GNUC__)
 #define RSWA_API __attribute__((visibility("default")))
@@ -439,6 +439,34 @@ RSWA_API rswa_status_t rswa_probe_stream_read(const void *buf, size_t bytes, flo
  * holds under matrix load, the practical ceiling of the packed kernels.
  */
 RSWA_API rswa_status_t rswa_probe_mfma(float *sink, int32_t workgroups, int32_t iters, void *stream);
+
+/*
+ * Measurement helper, not part of the attention path: per-CU rates of the units
+ * the packed kernels lean on besides the matrix cores, in shader-clock cycles.
+ * `workgroups` workgroups of 8 waves (0 picks 256: one per CU, which their
+ * 96 KB of LDS enforces; two waves per SIMD, the packed forward's count) each
+ * run `iters` rounds of one kind of instruction after a barrier and record the
+ * cycles the rounds took (s_memtime on wave 0):
+ *   RSWA_PROBE_LDS_B128 (0): 16 ds_read_b128 row-fragment reads per wave and
+ *       round (16 KB), the forward's K-fragment pattern;
+ *   RSWA_PROBE_LDS_TR16 (1): 32 ds_read_b64_tr_b16 transposing reads per wave and
+ *       round (16 KB), the forward's V^T pattern;
+ *   RSWA_PROBE_EXP (2): 8 independent v_exp_f32 per wave and round;
+ *   RSWA_PROBE_FMA (3): 8 independent v_fma_f32 per wave and round.
+ * out: device uint32 [2 * workgroups]: out[2 g] = cycles of workgroup g,
+ * out[2 g + 1] = a fold of its results (kept so the work is not optimised away).
+ * LDS bytes per clock per CU = 8 waves * iters * 16 KB / cycles;
+ * cycles per wave instruction per SIMD = cycles / (2 waves * iters * 8).
+ * Returns RSWA_ERR_SHAPE for workgroups < 0, iters < 1 or an unknown kind.
+ */
+enum {
+  RSWA_PROBE_LDS_B128 = 0,
+  RSWA_PROBE_LDS_TR16 = 1,
+  RSWA_PROBE_EXP = 2,
+  RSWA_PROBE_FMA = 3
+};
+RSWA_API rswa_status_t rswa_probe_cu(uint32_t *out, int32_t workgroups, int32_t iters, int32_t kind,
+                                     void *stream);
 
 /*
  * Synchronise `stream`, read the cache's device error word into *flags

@@ -48,7 +48,7 @@ EXPORTED = ("rswa_abi_version", "rswa_status_str", "rswa_cache_init", "rswa_appe
             "rswa_masked_attn_bwd", "rswa_masked_bwd_varlen_workspace_size",
             "rswa_masked_attn_bwd_varlen", "rswa_decode_graph_create", "rswa_decode_graph_launch",
             "rswa_decode_graph_destroy", "rswa_probe_stream_read", "rswa_probe_mfma",
-            "rswa_check_device_error")
+            "rswa_probe_cu", "rswa_check_device_error")
 
 
 class RswaError(RuntimeError):
@@ -111,6 +111,7 @@ def _lib() -> ctypes.CDLL:
             "rswa_decode_graph_destroy": (I32, [P]),
             "rswa_probe_stream_read": (I32, [P, SZ, P, I32, P]),
             "rswa_probe_mfma": (I32, [P, I32, I32, P]),
+            "rswa_probe_cu": (I32, [P, I32, I32, I32, P]),
             "rswa_check_device_error": (I32, [D, ctypes.POINTER(I32), P]),
         }
         for name, (res, args) in sig.items():
@@ -323,6 +324,15 @@ def rswa_probe_stream_read(buf, nbytes: int, sink, workgroups: int = 0, stream=N
 def rswa_probe_mfma(sink, workgroups: int = 0, iters: int = 4096, stream=None, check=True) -> int:
     st = _lib().rswa_probe_mfma(_ptr(sink), int(workgroups), int(iters), _stream(stream))
     return _check(st, "rswa_probe_mfma") if check else st
+
+
+RSWA_PROBE_LDS_B128, RSWA_PROBE_LDS_TR16, RSWA_PROBE_EXP, RSWA_PROBE_FMA = 0, 1, 2, 3
+
+
+def rswa_probe_cu(out, workgroups: int = 0, iters: int = 1024, kind: int = RSWA_PROBE_LDS_B128, stream=None,
+                  check=True) -> int:
+    st = _lib().rswa_probe_cu(_ptr(out), int(workgroups), int(iters), int(kind), _stream(stream))
+    return _check(st, "rswa_probe_cu") if check else st
 
 
 def rswa_check_device_error(desc: CacheDesc, stream=None) -> int:

@@ -685,6 +685,15 @@ rswa_status_t rswa_probe_mfma(float *sink, int32_t workgroups, int32_t iters, vo
   return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
 }
 
+rswa_status_t rswa_probe_cu(uint32_t *out, int32_t workgroups, int32_t iters, int32_t kind, void *stream) {
+  if (out == nullptr) return RSWA_ERR_NULL;
+  if (workgroups < 0 || iters < 1 || kind < RSWA_PROBE_LDS_B128 || kind > RSWA_PROBE_FMA) return RSWA_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(out) & 3u) != 0) return RSWA_ERR_ALIGN;
+  const hipError_t e = launch_probe_cu(out, workgroups == 0 ? 256 : workgroups, iters, kind,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
+}
+
 rswa_status_t rswa_check_device_error(const rswa_cache_t *cache, int32_t *flags, void *stream) {
   if (cache == nullptr || cache->error == nullptr || flags == nullptr) return RSWA_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -160,5 +160,6 @@ hipError_t launch_masked_bwd(const MaskedBwdParams &p, hipStream_t s);
 hipError_t launch_clear_word(int32_t *word, hipStream_t s);
 hipError_t launch_probe_read(const void *buf, size_t bytes, float *sink, int32_t workgroups, hipStream_t s);
 hipError_t launch_probe_mfma(float *sink, int32_t workgroups, int32_t iters, hipStream_t s);
+hipError_t launch_probe_cu(uint32_t *out, int32_t workgroups, int32_t iters, int32_t kind, hipStream_t s);
 
 }  // namespace rswa

@@ -241,6 +241,16 @@ def test_probe_mfma_argument_checks():
     assert pm(sink=A + 2) == rs.RSWA_ERR_ALIGN
 
 
+def test_probe_cu_argument_checks():
+    pc = lambda **kw: rs.rswa_probe_cu(**{**dict(out=A, workgroups=0, iters=16, kind=0), **kw}, check=False)
+    assert pc(out=None) == rs.RSWA_ERR_NULL
+    assert pc(workgroups=-1) == rs.RSWA_ERR_SHAPE
+    assert pc(iters=0) == rs.RSWA_ERR_SHAPE
+    assert pc(kind=-1) == rs.RSWA_ERR_SHAPE
+    assert pc(kind=4) == rs.RSWA_ERR_SHAPE
+    assert pc(out=A + 2) == rs.RSWA_ERR_ALIGN
+
+
 def test_masked_bwd_workspace_size():
     ws = rs.rswa_masked_bwd_workspace_size
     assert ws(-1, 0, 2) == 0
