@@ -48,6 +48,20 @@ def decode_bytes(B, H, d, L, n, T, elt=2):
     return B * H * (L + min(n, T)) * d * elt * 2 + 4 * B * H * d * elt
 
 
+def masked_tile_flops(N, L_m, n, H, prefix_full=False):
+    """FLOP the packed forward's matrix products execute (d = 128): every 64-key block that meets a
+    128-row query block's reference range or window range is multiplied whole, 4 waves x 32 products
+    of 32768 FLOP (16 for S^T, 16 for O^T); the algorithmic count takes visible pairs only."""
+    blocks = 0
+    for q0 in range(0, N, 128):
+        q_end = min(N, q0 + 128)
+        pre_hi = L_m if (prefix_full and q0 < L_m) else min(L_m, q_end)
+        win_lo = max(L_m, max(q0, L_m) - n + 1)
+        win_hi = q_end if q_end > L_m else win_lo
+        blocks += (pre_hi + 63) // 64 + (win_hi - win_lo + 63) // 64
+    return blocks * H * 4 * 32 * 32768
+
+
 def masked_flops(N, L_m, n, H, d, prefix_full=False):
     """4 d FLOP per visible (query, key) pair of the two-segment mask."""
     pre = L_m * L_m if prefix_full else L_m * (L_m + 1) // 2
@@ -474,8 +488,10 @@ def main():
             ms_m = med3(run, 20)
             fl = masked_flops(mw.seq_len, mw.ref_len, mw.window, mw.heads, mw.head_dim,
                               mode == rs.RSWA_PREFIX_FULL)
+            tile = masked_tile_flops(mw.seq_len, mw.ref_len, mw.window, mw.heads, mode == rs.RSWA_PREFIX_FULL)
             masked[name] = {"ms": ms_m, "algorithmic_flop": fl, "TFLOPs": fl / (ms_m * 1e-3) / 1e12,
-                            "frac_of_bf16_peak": fl / (ms_m * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+                            "frac_of_bf16_peak": fl / (ms_m * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                            "tile_flop": tile, "tile_over_algorithmic": tile / fl}
         # packed 32K backward (dQ, dK, dV) of the causal-prefix forward
         Gd = to_d(wl.packed_dout(mw))
         lse = torch.empty((mw.heads, mw.seq_len), dtype=torch.float32, device="cuda")
