@@ -110,7 +110,8 @@ def event_time_ms(fn, iters, stream):
 def cpu_baseline(w, kref, vref, T):
     """Time the oracle on every (sequence, head) of decode step T (all B x H pairs, the
     whole step) on the host's cores: one worker process per core, BLAS on one thread
-    each, inputs in shared memory before the clock starts."""
+    each, inputs in shared memory before the clock starts. Returns the timing line and
+    the oracle's outputs of that step, [B][H][d] float64."""
     import oracle.pool as opool
     import workloads as wl
     with opool.SharedArrays() as arrays:
@@ -124,10 +125,11 @@ def cpu_baseline(w, kref, vref, T):
         with opool.OraclePool(arrays) as pool:
             pool.map(opool.ready, range(4 * pool.processes))   # every worker up before timing
             t0 = time.perf_counter()
-            pool.map(opool.decode_sequence_job, tasks)
+            res = pool.map(opool.decode_sequence_job, tasks)
             el = time.perf_counter() - t0
             cores = pool.processes
-    return {"value": w.batch / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    ref = np.stack([r[T] for r in res])
+    return ref, {"value": w.batch / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"the whole 40-page decode step T={T} (steady state, window full): all "
                       f"{w.batch * w.heads} (sequence, head) pairs in {el:.1f} s wall on {cores} worker "
                       f"processes (one per host core, BLAS on one thread each; {cores * el:.0f} core-seconds); "
@@ -355,6 +357,7 @@ def main():
     progress(f"window filled and {W} warm-up steps run; timing {K} steps")
     ms = event_time_ms(lambda i: step(fill + W + i), K, stream)
     ms_per_step = ms / K
+    out_last_timed = out.clone()                 # output of step t_first + K - 1
     # the same number of further steps, each between its own pair of events
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     for i in range(K):
@@ -406,6 +409,19 @@ def main():
                      "achievable_read_GBps": achievable, "frac_of_achievable": achieved / achievable},
         "device": device_facts(torch),
     }
+    # cache image after the last step (bit for bit): the window slots hold outputs
+    # T_last - n + 1 .. T_last at slot L_m + ((t - 1) mod n); ks, vs hold every step's k, v
+    t_last = steps_total
+    ts = torch.arange(t_last - n + 1, t_last + 1, device="cuda")
+    per_seq = H * (L + n) * d
+    assert torch.equal(cache.seq_base.cpu(), torch.arange(B, dtype=torch.int64) * per_seq)
+    mism = 0
+    for pool, src in ((cache.k, ks), (cache.v, vs)):
+        win = pool[:B * per_seq].view(B, H, L + n, d)[:, :, L:, :][:, :, (ts - 1) % n, :]
+        want = src[ts - 1].permute(1, 2, 0, 3)
+        mism += int((win.view(torch.int16) != want.view(torch.int16)).any(-1).sum().item())
+    result["parity"] = {"cache_window_slot_mismatches": mism, "cache_step": t_last,
+                        "cache_rows_checked": 2 * B * H * n}
     del qs, ks, vs
 
     progress("contract line measured")
@@ -745,7 +761,15 @@ def main():
         result["per_step_curve"] = per_step_curve(torch, rs, w, stream, w.steps)
     if not args.no_cpu_baseline:
         progress("CPU oracle baseline")
-        result["cpu_baseline"] = cpu_baseline(w, kref, vref, t_first + K - 1)
+        ref, result["cpu_baseline"] = cpu_baseline(w, kref, vref, t_first + K - 1)
+        got = out_last_timed.float().cpu().numpy().astype(np.float64)
+        dlt = got - ref
+        pair_rel = (np.linalg.norm(dlt, axis=-1) / np.linalg.norm(ref, axis=-1)).max()
+        result["parity"]["oracle_step"] = t_first + K - 1
+        result["parity"]["max_abs"] = float(np.abs(dlt).max())
+        result["parity"]["rel_l2"] = float(np.linalg.norm(dlt) / np.linalg.norm(ref))
+        result["parity"]["worst_pair_rel_l2"] = float(pair_rel)
+        result["parity"]["bound"] = "max_abs <= 2e-2 and relative L2 <= 1e-2, pooled and per (sequence, head)"
     result["setup_s"] = setup_s
     print(json.dumps(result), flush=True)
 
