@@ -36,7 +36,6 @@ namespace {
 
 using namespace tile;
 
-
 // ---------------------------------------------------------------- pre-pass
 // nd[h][i] = -sum_d dO[i][h][d] O[i][h][d] and nls[h][i] = -lse[h][i] / scale (in
 // the units of the unscaled scores), stored so because the dK/dV products start
@@ -427,7 +426,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
     b_lo = s0;
   }
   const int nblocks = max(0, b_hi - b_lo);
-  const float *lse2_h = p.nls + (int64_t)h * p.n_pad + row0;
+  const float *nls_h = p.nls + (int64_t)h * p.n_pad + row0;
   const float *d_h = p.nd_row + (int64_t)h * p.n_pad + row0;
 
   // DMA of one 32-row query block: wave w fills rows 4 w .. 4 w + 3 of the Q and
@@ -449,7 +448,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
       // rows past the sequence's end repeat its last row, as the tile rows do
       // (their scores are masked, so P = dS = 0 whatever finite values sit here)
       const int rr = min(qb0 + (lane & 31), N - 1);
-      const float *src = lane < 32 ? lse2_h + rr : d_h + rr;
+      const float *src = lane < 32 ? nls_h + rr : d_h + rr;
       dma4(src, st_lds + (uint32_t)offsetof(DkdvStage, ld));  // lane L's dword lands at ld[L]
     }
   };
