@@ -59,7 +59,7 @@ typedef enum {
   RSWA_ERR_SHAPE = -2,       /* a size/shape argument is out of range               */
   RSWA_ERR_UNSUPPORTED = -3, /* valid but not implemented (dtype, head_dim, mode)   */
   RSWA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                    */
-  RSWA_ERR_CAPACITY = -5,    /* sizes would overflow 32-bit slot or 64-bit offsets  */
+  RSWA_ERR_CAPACITY = -5,    /* sizes would overflow the kernels' index arithmetic  */
   RSWA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required          */
   RSWA_ERR_STATE = -7,       /* device-side state was found invalid                 */
   RSWA_ERR_HIP = -8          /* the HIP runtime reported an error                   */
@@ -243,6 +243,10 @@ RSWA_API rswa_status_t rswa_decode_attn_noalloc(const rswa_cache_t *cache, const
  * before scaling, which needs a positive scale; a negative one is rejected
  * with RSWA_ERR_SHAPE here and in every other packed call (varlen, prefill and
  * both backward calls). The decode calls accept any finite scale.
+ * Sizes: seq_len * num_heads * head_dim below 2^31 and num_heads below 2^16
+ * (the kernels' offsets are 32-bit, their row offsets 24-bit products), else
+ * RSWA_ERR_CAPACITY; the same limits hold for every other packed call (with
+ * total_tokens, or the cache's heads for rswa_prefill).
  */
 RSWA_API rswa_status_t rswa_masked_attn(const void *q, const void *k, const void *v, void *out,
                                float *lse, int32_t seq_len, int32_t ref_len, int32_t window,

@@ -26,6 +26,14 @@ bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// The packed kernels (head_dim 128) form element offsets in 32 bits and each DMA
+// row offset as a 24-bit product (row number times the row pitch of 256 H
+// bytes): the tokens x heads x 128 elements stay below 2^31 and the heads below
+// 2^16, which also keeps every row number below 2^24.
+bool packed_sizes_fit(int64_t tokens, int64_t heads) {
+  return tokens * heads * 128 < ((int64_t)1 << 31) && heads < ((int64_t)1 << 16);
+}
+
 // Host-visible checks of a cache descriptor (device arrays are checked by the kernels).
 rswa_status_t check_cache(const rswa_cache_t *c) {
   if (c == nullptr) return RSWA_ERR_NULL;
@@ -343,8 +351,7 @@ rswa_status_t rswa_masked_attn(const void *q, const void *k, const void *v, void
   if (dtype != RSWA_BF16 || head_dim != 128) return RSWA_ERR_UNSUPPORTED;
   if (prefix_mode != RSWA_PREFIX_CAUSAL && prefix_mode != RSWA_PREFIX_FULL)
     return RSWA_ERR_UNSUPPORTED;
-  // element offsets inside the kernel are 32-bit
-  if ((int64_t)seq_len * num_heads * head_dim >= ((int64_t)1 << 31)) return RSWA_ERR_CAPACITY;
+  if (!packed_sizes_fit(seq_len, num_heads)) return RSWA_ERR_CAPACITY;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RSWA_ERR_ALIGN;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RSWA_ERR_ALIGN;
   if (!isfinite(scale) || scale < 0.f) return RSWA_ERR_SHAPE;  // see rswa_masked_attn
@@ -382,7 +389,7 @@ rswa_status_t rswa_masked_attn_varlen(const void *q, const void *k, const void *
   if (dtype != RSWA_BF16 || head_dim != 128) return RSWA_ERR_UNSUPPORTED;
   if (prefix_mode != RSWA_PREFIX_CAUSAL && prefix_mode != RSWA_PREFIX_FULL)
     return RSWA_ERR_UNSUPPORTED;
-  if ((int64_t)total_tokens * num_heads * head_dim >= ((int64_t)1 << 31)) return RSWA_ERR_CAPACITY;
+  if (!packed_sizes_fit(total_tokens, num_heads)) return RSWA_ERR_CAPACITY;
   if ((int64_t)num_seqs * num_heads * ((max_seq_len + 127) / 128) >= ((int64_t)1 << 31))
     return RSWA_ERR_CAPACITY;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RSWA_ERR_ALIGN;
@@ -422,8 +429,7 @@ rswa_status_t rswa_prefill(const rswa_cache_t *cache, const void *q, const void 
   if (total_tokens < 0 || max_seq_len < 0) return RSWA_ERR_SHAPE;
   if (prefix_mode != RSWA_PREFIX_CAUSAL && prefix_mode != RSWA_PREFIX_FULL)
     return RSWA_ERR_UNSUPPORTED;
-  if ((int64_t)total_tokens * cache->num_heads * cache->head_dim >= ((int64_t)1 << 31))
-    return RSWA_ERR_CAPACITY;
+  if (!packed_sizes_fit(total_tokens, cache->num_heads)) return RSWA_ERR_CAPACITY;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RSWA_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return RSWA_ERR_ALIGN;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RSWA_ERR_ALIGN;
@@ -482,7 +488,7 @@ rswa_status_t rswa_masked_attn_bwd(const void *q, const void *k, const void *v, 
   if (dtype != RSWA_BF16 || head_dim != 128) return RSWA_ERR_UNSUPPORTED;
   if (prefix_mode != RSWA_PREFIX_CAUSAL && prefix_mode != RSWA_PREFIX_FULL)
     return RSWA_ERR_UNSUPPORTED;
-  if ((int64_t)seq_len * num_heads * head_dim >= ((int64_t)1 << 31)) return RSWA_ERR_CAPACITY;
+  if (!packed_sizes_fit(seq_len, num_heads)) return RSWA_ERR_CAPACITY;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return RSWA_ERR_ALIGN;
@@ -551,7 +557,7 @@ rswa_status_t rswa_masked_attn_bwd_varlen(const void *q, const void *k, const vo
   if (dtype != RSWA_BF16 || head_dim != 128) return RSWA_ERR_UNSUPPORTED;
   if (prefix_mode != RSWA_PREFIX_CAUSAL && prefix_mode != RSWA_PREFIX_FULL)
     return RSWA_ERR_UNSUPPORTED;
-  if ((int64_t)total_tokens * num_heads * head_dim >= ((int64_t)1 << 31)) return RSWA_ERR_CAPACITY;
+  if (!packed_sizes_fit(total_tokens, num_heads)) return RSWA_ERR_CAPACITY;
   if ((int64_t)num_seqs * num_heads * ((max_seq_len + 127) / 128) >= ((int64_t)1 << 31))
     return RSWA_ERR_CAPACITY;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||

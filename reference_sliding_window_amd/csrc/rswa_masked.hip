@@ -187,7 +187,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
   // instructions per wave. The tensor's base stays in scalar registers; each
   // lane adds the byte offset of its row (clamped to the segment's last row)
   // and of its swizzled 16-byte chunk, which is fixed for the kernel. Byte
-  // offsets fit in 32 bits (the host rejects tensors of 2^31 elements or more).
+  // offsets fit in 32 bits and the row product in the 24-bit multiplier (the
+  // host rejects tensors of 2^31 elements or more and 2^16 heads or more).
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   uint32_t c16[4];
 #pragma unroll

@@ -170,7 +170,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(MaskedBwdParams p) {
   // DMA of one 32-key block: wave w fills rows 8 w .. 8 w + 7 of the K and V
   // tiles, 4 instructions per wave and block. Tensor bases stay scalar; a lane
   // adds the byte offset of its row (clamped to the segment's last row) and of
-  // its swizzled 16-byte chunk (fixed for the kernel).
+  // its swizzled 16-byte chunk (fixed for the kernel). Byte offsets fit in 32
+  // bits and the row product in the 24-bit multiplier (the host rejects tensors
+  // of 2^31 elements or more and 2^16 heads or more).
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t stride2 = 2u * stride;
   uint32_t c16[2];
@@ -431,7 +433,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(MaskedBwdParams p) {
 
   // DMA of one 32-row query block: wave w fills rows 4 w .. 4 w + 3 of the Q and
   // dO tiles (2 instructions) and, with its lanes 8 w .. 8 w + 7, an eighth of
-  // the lse/D strip (1 instruction): 3 per wave and block.
+  // the lse/D strip (1 instruction): 3 per wave and block. Row offsets as in
+  // the dQ kernel's DMA (32-bit, from a 24-bit product).
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t stride2 = 2u * stride;
   const uint32_t c16 = 16u * (uint32_t)((lane & 15) ^ chunk_swz(4 * wave + (lane >> 4)));

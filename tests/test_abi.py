@@ -154,6 +154,7 @@ def test_masked_argument_checks():
     assert m(scale=math.nan) == rs.RSWA_ERR_SHAPE
     assert m(lse=A + 2) == rs.RSWA_ERR_ALIGN
     assert m(seq_len=2 ** 20, ref_len=0, num_heads=16) == rs.RSWA_ERR_CAPACITY
+    assert m(seq_len=2, ref_len=0, num_heads=2 ** 16) == rs.RSWA_ERR_CAPACITY   # 24-bit row products
     assert m(seq_len=0, ref_len=0) == rs.RSWA_OK   # nothing to do, nothing enqueued
 
 
@@ -172,6 +173,7 @@ def test_varlen_argument_checks():
     assert m(dtype=rs.RSWA_FP32) == rs.RSWA_ERR_UNSUPPORTED
     assert m(prefix_mode=9) == rs.RSWA_ERR_UNSUPPORTED
     assert m(total_tokens=2 ** 20, num_heads=16) == rs.RSWA_ERR_CAPACITY
+    assert m(total_tokens=2, max_seq_len=2, num_heads=2 ** 16) == rs.RSWA_ERR_CAPACITY
     assert m(q=A + 8) == rs.RSWA_ERR_ALIGN
     assert m(cu_seqlens=A + 2) == rs.RSWA_ERR_ALIGN
     assert m(lse=A + 1) == rs.RSWA_ERR_ALIGN
@@ -195,6 +197,7 @@ def test_prefill_argument_checks():
     assert p(max_seq_len=-3) == rs.RSWA_ERR_SHAPE
     assert p(prefix_mode=5) == rs.RSWA_ERR_UNSUPPORTED
     assert p(total_tokens=2 ** 22) == rs.RSWA_ERR_CAPACITY
+    assert p(desc=good_desc(batch=1, num_heads=2 ** 16), total_tokens=2, max_seq_len=2) == rs.RSWA_ERR_CAPACITY
     assert p(out=A + 4) == rs.RSWA_ERR_ALIGN
     assert p(cu_seqlens=A + 1) == rs.RSWA_ERR_ALIGN
     assert p(scale=math.inf) == rs.RSWA_ERR_SHAPE
@@ -288,6 +291,7 @@ def test_masked_bwd_argument_checks():
     assert b(prefix_mode=2) == rs.RSWA_ERR_UNSUPPORTED
     assert b(scale=math.inf) == rs.RSWA_ERR_SHAPE
     assert b(seq_len=2 ** 20, ref_len=0, num_heads=16) == rs.RSWA_ERR_CAPACITY
+    assert b(seq_len=2, ref_len=0, num_heads=2 ** 16) == rs.RSWA_ERR_CAPACITY
     assert b(workspace=None, workspace_bytes=0) == rs.RSWA_ERR_NULL
     assert b(workspace_bytes=ws - 1) == rs.RSWA_ERR_WORKSPACE
     assert b(workspace=A + 4) == rs.RSWA_ERR_ALIGN
@@ -327,6 +331,7 @@ def test_varlen_bwd_argument_checks():
     assert b(prefix_mode=2) == rs.RSWA_ERR_UNSUPPORTED
     assert b(scale=math.nan) == rs.RSWA_ERR_SHAPE
     assert b(total_tokens=2 ** 20, num_heads=16) == rs.RSWA_ERR_CAPACITY
+    assert b(total_tokens=2, max_seq_len=2, num_heads=2 ** 16) == rs.RSWA_ERR_CAPACITY
     assert b(num_seqs=2 ** 20, max_seq_len=2 ** 20, num_heads=16, total_tokens=1) == rs.RSWA_ERR_CAPACITY
     assert b(workspace=None, workspace_bytes=0) == rs.RSWA_ERR_NULL
     assert b(workspace_bytes=ws - 1) == rs.RSWA_ERR_WORKSPACE
