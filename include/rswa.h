@@ -307,7 +307,8 @@ RSWA_API rswa_status_t rswa_prefill(const rswa_cache_t *cache, const void *q, co
 
 /*
  * Bytes of device workspace rswa_masked_attn_bwd needs for these sizes and
- * num_parts (0 = the library's choice, as in the call). 0 for invalid sizes.
+ * num_parts (0 = the library's choice, as in the call). 0 for invalid sizes
+ * and for sizes the call rejects with RSWA_ERR_CAPACITY.
  */
 RSWA_API size_t rswa_masked_bwd_workspace_size(int32_t seq_len, int32_t ref_len, int32_t num_heads,
                                                int32_t num_parts);
@@ -349,7 +350,8 @@ RSWA_API rswa_status_t rswa_masked_attn_bwd(const void *q, const void *k, const 
 
 /*
  * Bytes of device workspace rswa_masked_attn_bwd_varlen needs for a pack of
- * total_tokens rows. 0 for invalid sizes.
+ * total_tokens rows. 0 for invalid sizes and for sizes the call rejects with
+ * RSWA_ERR_CAPACITY.
  */
 RSWA_API size_t rswa_masked_bwd_varlen_workspace_size(int32_t total_tokens, int32_t num_heads);
 

@@ -468,7 +468,7 @@ rswa_status_t rswa_prefill(const rswa_cache_t *cache, const void *q, const void 
 size_t rswa_masked_bwd_workspace_size(int32_t seq_len, int32_t ref_len, int32_t num_heads,
                                       int32_t num_parts) {
   if (seq_len < 0 || ref_len < 0 || ref_len > seq_len || num_heads < 1 || num_parts < 0 ||
-      num_parts > kMaxBwdParts)
+      num_parts > kMaxBwdParts || !packed_sizes_fit(seq_len, num_heads))
     return 0;
   const BwdPlan b = plan_masked_bwd(seq_len, ref_len, num_heads, num_parts);
   return b.bytes_rows + b.bytes_parts;
@@ -534,7 +534,7 @@ rswa_status_t rswa_masked_attn_bwd(const void *q, const void *k, const void *v, 
 }
 
 size_t rswa_masked_bwd_varlen_workspace_size(int32_t total_tokens, int32_t num_heads) {
-  if (total_tokens < 0 || num_heads < 1) return 0;
+  if (total_tokens < 0 || num_heads < 1 || !packed_sizes_fit(total_tokens, num_heads)) return 0;
   const size_t n_pad = ((size_t)total_tokens + 31) / 32 * 32;
   return 2 * (size_t)num_heads * n_pad * sizeof(float);
 }

@@ -262,6 +262,8 @@ def test_masked_bwd_workspace_size():
     assert ws(10, 5, 2, -1) == 0
     assert ws(10, 5, 2, 65) == 0
     assert ws(0, 0, 2) == 0
+    assert ws(2 ** 31 - 1, 0, 1) == 0   # sizes the call rejects with RSWA_ERR_CAPACITY
+    assert ws(2, 0, 2 ** 16) == 0
     # one part: two float arrays [H][roundup(N, 32)]
     assert ws(1, 1, 2, 1) == 2 * 2 * 32 * 4
     assert ws(300, 40, 3, 1) == 2 * 3 * 320 * 4
@@ -307,6 +309,8 @@ def test_masked_bwd_varlen_workspace_size():
     assert rs.rswa_masked_bwd_varlen_workspace_size(0, 3) == 0
     assert rs.rswa_masked_bwd_varlen_workspace_size(-1, 2) == 0
     assert rs.rswa_masked_bwd_varlen_workspace_size(64, 0) == 0
+    assert rs.rswa_masked_bwd_varlen_workspace_size(2 ** 20, 16) == 0   # rejected by the call
+    assert rs.rswa_masked_bwd_varlen_workspace_size(2, 2 ** 16) == 0
 
 
 def test_varlen_bwd_argument_checks():
