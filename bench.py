@@ -140,11 +140,17 @@ def progress(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def device_facts(torch):
+def device_facts(torch, rs):
+    """The device as torch and the HIP runtime (through the library) report it: the unit counts and
+    sizes the roofline figures assume, and the peak clocks."""
     p = torch.cuda.get_device_properties(0)
+    f = rs.rswa_device_facts(torch.cuda.current_device())
     return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
             "total_memory_GiB": round(p.total_memory / 2 ** 30, 1),
-            "l2_cache_MiB_reported": round(getattr(p, "L2_cache_size", 0) / 2 ** 20, 1)}
+            "l2_cache_MiB_reported": round(getattr(p, "L2_cache_size", 0) / 2 ** 20, 1),
+            "lds_KiB_per_cu": f["lds_bytes_per_cu"] / 1024, "wave_size": f["wave_size"],
+            "peak_shader_clock_MHz": f["clock_khz"] / 1000, "peak_memory_clock_MHz": f["mem_clock_khz"] / 1000,
+            "memory_bus_width_bits": f["mem_bus_bits"]}
 
 
 def probe_read_GBps(torch, rs, stream, nbytes=4 << 30):
@@ -407,7 +413,7 @@ def main():
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "traffic_steps": "steady state (all L_m + n slots visible), as the timed steps",
                      "achievable_read_GBps": achievable, "frac_of_achievable": achieved / achievable},
-        "device": device_facts(torch),
+        "device": device_facts(torch, rs),
     }
     # cache image after the last step (bit for bit): the window slots hold outputs
     # T_last - n + 1 .. T_last at slot L_m + ((t - 1) mod n); ks, vs hold every step's k, v

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define RSWA_ABI_VERSION 8
+#define RSWA_ABI_VERSION 9
 
 #if defined(__GNUC__)
 #define RSWA_API __attribute__((visibility("default")))
@@ -473,6 +473,30 @@ enum {
 };
 RSWA_API rswa_status_t rswa_probe_cu(uint32_t *out, int32_t workgroups, int32_t iters, int32_t kind,
                                      void *stream);
+
+/*
+ * Measurement helper, not part of the attention path: facts of HIP device
+ * `device` as the runtime reports them, so that a measurement record can state
+ * the hardware it ran on. Writes min(count, RSWA_FACT_COUNT) host int64 values
+ * to `out`, indexed by the RSWA_FACT_* constants: compute units, LDS bytes per
+ * compute unit, L2 bytes (as reported; one XCD's share on a multi-XCD part),
+ * peak shader clock (kHz), peak memory clock (kHz), memory bus width (bits),
+ * global memory bytes, wavefront size. Host-synchronous; enqueues nothing.
+ * Returns RSWA_ERR_NULL for a NULL out, RSWA_ERR_SHAPE for device < 0 or
+ * count < 1, RSWA_ERR_HIP when the runtime cannot report the device.
+ */
+enum {
+  RSWA_FACT_COMPUTE_UNITS = 0,
+  RSWA_FACT_LDS_BYTES_PER_CU = 1,
+  RSWA_FACT_L2_BYTES = 2,
+  RSWA_FACT_CLOCK_KHZ = 3,
+  RSWA_FACT_MEM_CLOCK_KHZ = 4,
+  RSWA_FACT_MEM_BUS_BITS = 5,
+  RSWA_FACT_GLOBAL_MEM_BYTES = 6,
+  RSWA_FACT_WAVE_SIZE = 7,
+  RSWA_FACT_COUNT = 8
+};
+RSWA_API rswa_status_t rswa_device_facts(int32_t device, int64_t *out, int32_t count);
 
 /*
  * Synchronise `stream`, read the cache's device error word into *flags

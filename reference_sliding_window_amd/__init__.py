@@ -48,7 +48,7 @@ EXPORTED = ("rswa_abi_version", "rswa_status_str", "rswa_cache_init", "rswa_appe
             "rswa_masked_attn_bwd", "rswa_masked_bwd_varlen_workspace_size",
             "rswa_masked_attn_bwd_varlen", "rswa_decode_graph_create", "rswa_decode_graph_launch",
             "rswa_decode_graph_destroy", "rswa_probe_stream_read", "rswa_probe_mfma",
-            "rswa_probe_cu", "rswa_check_device_error")
+            "rswa_probe_cu", "rswa_device_facts", "rswa_check_device_error")
 
 
 class RswaError(RuntimeError):
@@ -112,6 +112,7 @@ def _lib() -> ctypes.CDLL:
             "rswa_probe_stream_read": (I32, [P, SZ, P, I32, P]),
             "rswa_probe_mfma": (I32, [P, I32, I32, P]),
             "rswa_probe_cu": (I32, [P, I32, I32, I32, P]),
+            "rswa_device_facts": (I32, [I32, ctypes.POINTER(ctypes.c_int64), I32]),
             "rswa_check_device_error": (I32, [D, ctypes.POINTER(I32), P]),
         }
         for name, (res, args) in sig.items():
@@ -333,6 +334,17 @@ def rswa_probe_cu(out, workgroups: int = 0, iters: int = 1024, kind: int = RSWA_
                   check=True) -> int:
     st = _lib().rswa_probe_cu(_ptr(out), int(workgroups), int(iters), int(kind), _stream(stream))
     return _check(st, "rswa_probe_cu") if check else st
+
+
+DEVICE_FACTS = ("compute_units", "lds_bytes_per_cu", "l2_bytes", "clock_khz", "mem_clock_khz",
+                "mem_bus_bits", "global_mem_bytes", "wave_size")
+
+
+def rswa_device_facts(device: int = 0) -> dict:
+    """The HIP runtime's facts of one device, keyed by DEVICE_FACTS."""
+    out = (ctypes.c_int64 * len(DEVICE_FACTS))()
+    _check(_lib().rswa_device_facts(int(device), out, len(DEVICE_FACTS)), "rswa_device_facts")
+    return dict(zip(DEVICE_FACTS, (int(x) for x in out)))
 
 
 def rswa_check_device_error(desc: CacheDesc, stream=None) -> int:

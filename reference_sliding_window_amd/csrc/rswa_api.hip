@@ -700,6 +700,20 @@ rswa_status_t rswa_probe_cu(uint32_t *out, int32_t workgroups, int32_t iters, in
   return e == hipSuccess ? RSWA_OK : RSWA_ERR_HIP;
 }
 
+rswa_status_t rswa_device_facts(int32_t device, int64_t *out, int32_t count) {
+  if (out == nullptr) return RSWA_ERR_NULL;
+  if (device < 0 || count < 1) return RSWA_ERR_SHAPE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return RSWA_ERR_HIP;
+  const int64_t facts[RSWA_FACT_COUNT] = {
+      prop.multiProcessorCount,          (int64_t)prop.maxSharedMemoryPerMultiProcessor,
+      prop.l2CacheSize,                  prop.clockRate,
+      prop.memoryClockRate,              prop.memoryBusWidth,
+      (int64_t)prop.totalGlobalMem,      prop.warpSize};
+  for (int i = 0; i < count && i < RSWA_FACT_COUNT; ++i) out[i] = facts[i];
+  return RSWA_OK;
+}
+
 rswa_status_t rswa_check_device_error(const rswa_cache_t *cache, int32_t *flags, void *stream) {
   if (cache == nullptr || cache->error == nullptr || flags == nullptr) return RSWA_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -244,6 +244,15 @@ def test_probe_mfma_argument_checks():
     assert pm(sink=A + 2) == rs.RSWA_ERR_ALIGN
 
 
+def test_device_facts_argument_checks():
+    lib = rs._lib()
+    buf = (ctypes.c_int64 * 8)()
+    assert lib.rswa_device_facts(0, None, 8) == rs.RSWA_ERR_NULL
+    assert lib.rswa_device_facts(-1, buf, 8) == rs.RSWA_ERR_SHAPE
+    assert lib.rswa_device_facts(0, buf, 0) == rs.RSWA_ERR_SHAPE
+    assert len(rs.DEVICE_FACTS) == int(re.search(r"RSWA_FACT_COUNT = (\d+)", open(HEADER).read()).group(1))
+
+
 def test_probe_cu_argument_checks():
     pc = lambda **kw: rs.rswa_probe_cu(**{**dict(out=A, workgroups=0, iters=16, kind=0), **kw}, check=False)
     assert pc(out=None) == rs.RSWA_ERR_NULL

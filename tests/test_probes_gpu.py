@@ -1,8 +1,9 @@
 """The measurement helpers the bench reports beside the kernels (not on the
 attention path) run through the C ABI and give sane figures: the streaming-read
 probe touches every workgroup's sink entry, the matrix-core probe's folds are
-finite, and the per-CU probe records positive cycle counts for every kind, with
-LDS rates and instruction costs inside what any CDNA part can do."""
+finite, the per-CU probe records positive cycle counts for every kind, with
+LDS rates and instruction costs inside what any CDNA part can do, and the
+device facts agree with what torch reports of the same device."""
 import numpy as np
 import pytest
 import torch
@@ -47,3 +48,15 @@ def test_cu_probe(kind):
         print(f"cycles per wave instruction per SIMD: {cpi:.2f}", flush=True)
         assert 1 <= cpi <= 64
         assert (o[1::2] != 0).any()          # the fold of the arithmetic results was written
+
+
+def test_device_facts():
+    print("\n[case] device facts", flush=True)
+    f = rs.rswa_device_facts(0)
+    p = torch.cuda.get_device_properties(0)
+    print(f, flush=True)
+    assert f["compute_units"] == p.multi_processor_count
+    assert f["global_mem_bytes"] == p.total_memory
+    assert f["wave_size"] == 64
+    assert f["lds_bytes_per_cu"] >= 64 * 1024
+    assert f["clock_khz"] > 0 and f["mem_clock_khz"] > 0 and f["mem_bus_bits"] > 0
