@@ -76,7 +76,7 @@ def check_grad(got: np.ndarray, ref: np.ndarray, what: str):
     """Gradient rule: max|diff| <= 2e-2 max(1, max|ref|) and relative L2 <= 1e-2, over
     the whole tensor and over each head (axis -2 of [rows][H][d]) on its own, so one
     wrong head cannot hide among the others. Not per row: the backward forms
-    D_i = dO_i . O_i from the forward's bf16 output (2^-9 relative), and for a row
+    D_i = dO_i . O_i from the forward's bf16 output (up to 2^-8 relative), and for a row
     that sees a few keys dS = P (dP - D) turns that into a few per cent of the
     row's own dQ where dP is close to D. Returns (max|diff|, worst per-head
     relative L2)."""

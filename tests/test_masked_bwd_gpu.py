@@ -7,9 +7,10 @@ and the kernels round P and dS to bf16 as matrix-core operands, so the error is
 relative to the gradient's magnitude: max|diff| <= 2e-2 * max(1, max|ref|) and
 ||diff||_2 / ||ref||_2 <= 1e-2, over each gradient tensor and over each head
 on its own (see gpu_util.check_grad). The log-sum-exp is fp32, but the forward sums
-the probabilities it has rounded to bf16 (each within 2^-9 relative), so its
-normaliser is within a factor 1 +- 2^-9 of the exact one:
-|diff| <= 2^-9 + 2e-4 + 1e-5 |ref| (the rest covers fp32 scores and exp2)."""
+the probabilities it has rounded to bf16 (8 significant bits: each within 2^-8
+relative of its fp32 value), so its normaliser is within a factor 1 +- 2^-8 of
+the exact one: |diff| <= 2^-8 + 2e-4 + 1e-5 |ref| (the rest covers fp32 scores
+and exp2)."""
 from __future__ import annotations
 
 import numpy as np
@@ -91,7 +92,7 @@ def test_forward_lse_every_row(N, L_m, n, mode):
     got = r.lse.cpu().numpy().astype(np.float64).T
     err = np.abs(got - ref)
     assert np.isfinite(got).all()
-    assert (err <= 2.0 ** -9 + 2e-4 + 1e-5 * np.abs(ref)).all(), f"lse max err {err.max():.3e}"
+    assert (err <= 2.0 ** -8 + 2e-4 + 1e-5 * np.abs(ref)).all(), f"lse max err {err.max():.3e}"
 
 
 def test_forward_lse_does_not_change_output():
@@ -228,8 +229,11 @@ def test_backward_32k_sampled_and_column_sums(mode):
     check_grad(dv_sum, g_sum, "sum_j dV_j vs sum_i dO_i")
     # sum_j dK_j vanishes in exact arithmetic; here each row's dS sums to a
     # rounding residue (the forward rounds P to bf16 for its normaliser and
-    # output, the backward rounds dS), so bound the sum by 2^-9 of the mass
-    # that cancels: sum_j |dK_j| per head and dimension.
+    # output, the backward rounds dS), each at most bf16's unit roundoff 2^-8
+    # of that row's mass. The rows round independently, so over 32K rows their
+    # sum grows like the square root of the count while the mass grows
+    # linearly: bound it by 2^-9 of the mass that cancels, sum_j |dK_j|, per
+    # head and dimension.
     dk_sum = dk.sum(axis=0)
     bound = 2.0 ** -9 * np.abs(dk).sum(axis=0)
     worst = float((np.abs(dk_sum) / bound).max())

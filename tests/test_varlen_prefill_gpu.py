@@ -77,7 +77,7 @@ def test_varlen_every_row_of_every_sample(mode):
         ref, ref_lse = sample_oracle(Q, K, V, r0, r1, L, n, mode)
         check_close(got[r0:r1], ref, "bf16", f"sample {s} (rows {r0}..{r1}, L={L})")
         err = np.abs(got_lse[:, r0:r1].T - ref_lse)
-        assert (err <= 2.0 ** -9 + 2e-4 + 1e-5 * np.abs(ref_lse)).all(), f"sample {s} lse {err.max():.3e}"
+        assert (err <= 2.0 ** -8 + 2e-4 + 1e-5 * np.abs(ref_lse)).all(), f"sample {s} lse {err.max():.3e}"
     assert torch.isnan(out[int(cu[-1]):].float()).all(), "rows outside every sample were written"
 
 
