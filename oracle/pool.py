@@ -32,7 +32,7 @@ _LIMITS = None
 
 
 def workers() -> int:
-    """Host cores this process may use, at most 16 (a one-GPU machine's share)."""
+    """Host cores this process may use, at most 16 (one GPU's share of the host's cores)."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
