@@ -83,12 +83,15 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
   // XCD-aware order: logical work item w -> (head, sample, query block). An XCD
   // takes a contiguous range of w: the query blocks of one (sample, head) share
   // its L2, and with heads outermost every XCD gets the same heads of every
-  // sample, so samples of different sizes do not unbalance the XCDs.
+  // sample, so samples of different sizes do not unbalance the XCDs. Within a
+  // (sample, head) the last query block comes first: with a causal prefix the
+  // later blocks see the most keys, and the cheap prefix blocks then fill the
+  // tail of the launch.
   int w = blockIdx.x;
   if ((G & 7) == 0) w = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   const int h = w / (p.num_seqs * nqb);
   const int sample = (w / nqb) % p.num_seqs;
-  const int q0 = (w % nqb) * kBM;
+  const int q0 = (nqb - 1 - w % nqb) * kBM;
   // One sample of the pack: rows [row0, row0 + N) with its own reference
   // length; no row sees another sample's keys.
   int row0 = 0, N = p.seq_len, Lm = p.ref_len;
@@ -100,8 +103,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParam
     N = row1 - row0;
     const bool pack_bad = row0 < 0 || row1 < row0 || row1 > p.seq_len || N > p.max_seq_len || Lm > N;
     if (p.cache_k != nullptr) {
-      // Prefill hand-off: the per-sequence checks of the cache calls; the
-      // first workgroup of the sequence publishes step[b] = T0 or the error.
+      // Prefill hand-off: the per-sequence checks of the cache calls; one
+      // workgroup of the sequence (head 0, work item 0 of its query blocks)
+      // publishes step[b] = T0 or the error.
       int err = pack_bad ? RSWA_DEVERR_PACK : 0;
       if (Lm < 0 || Lm > p.max_ref_len) err |= RSWA_DEVERR_REF_LEN;
       const int64_t cb = p.seq_base[sample];

@@ -86,12 +86,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(MaskedBwdParams p) {
   const int samples = p.cu_seqlens != nullptr ? p.num_seqs : 1;
   const int nqb = ((p.cu_seqlens != nullptr ? p.max_seq_len : p.seq_len) + kBMq - 1) / kBMq;
   const int G = samples * H * nqb;
-  // Work item w -> (head, sample, query block); an XCD takes a contiguous range of w.
+  // Work item w -> (head, sample, query block); an XCD takes a contiguous range of
+  // w, and within a (sample, head) the last query block (the most keys) comes first.
   int w = blockIdx.x;
   if ((G & 7) == 0) w = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   const int h = w / (samples * nqb);
   const int sample = (w / nqb) % samples;
-  const int q0 = (w % nqb) * kBMq;
+  const int q0 = (nqb - 1 - w % nqb) * kBMq;
   // One sample of a pack: rows [row0, row0 + N) with its own reference length.
   int row0 = 0, N = p.seq_len, Lm = p.ref_len;
   if (p.cu_seqlens != nullptr) {
