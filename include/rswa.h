@@ -16,8 +16,11 @@
  * KV cache (yhxrc.cn news article, section "R-SWA 如何穩住長程解碼？").
  *
  * General rules for every call
- *  - All tensor pointers are DEVICE pointers owned by the caller; the library
- *    allocates no memory and keeps no mutable global state.
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    allocates no device memory (rswa_decode_attn_noalloc uses a static buffer
+ *    reserved when the library loads) and no host memory except the handle of
+ *    rswa_decode_graph_create; its only mutable global state is that static
+ *    buffer and the per-device table of its addresses.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls
  *    only enqueue work on it and return; none synchronises except
  *    rswa_check_device_error.
@@ -153,7 +156,7 @@ RSWA_API rswa_status_t rswa_append_kv(const rswa_cache_t *cache, const void *k_n
  * cache (yhxrc page, "R-SWA 如何穩住長程解碼？"; 夜雨聆风 page, "为什么它能”无限”读下去？
  * 关键在 KV cache 恒定"). Equals rswa_decode_workspace_size(cache, 0) for a
  * descriptor with those sizes. Returns 0 for invalid sizes (batch or num_heads
- * < 1, head_dim not 64 or 128, max_len < 1).
+ * < 1, head_dim not 64 or 128, max_len < 1, batch * num_heads >= 2^30).
  */
 RSWA_API size_t rswa_workspace_size(int32_t batch, int32_t num_heads, int32_t head_dim,
                                     int32_t max_len);
