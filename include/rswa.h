@@ -240,7 +240,9 @@ RSWA_API rswa_status_t rswa_decode_attn_noalloc(const rswa_cache_t *cache, const
  * the probabilities are rounded to bf16 before the PV product.
  * lse: NULL, or device float [num_heads][seq_len] receiving each row's natural
  * log of the softmax normaliser, log sum_j exp(scale q_i.k_j) over the visible
- * keys (the input the backward pass needs).
+ * keys (the input the backward pass needs). The sum runs over the same
+ * bf16-rounded probabilities that enter PV, so lse is within about 2^-8 of the
+ * exact value (bf16 keeps 8 significant bits).
  * scale: 0 selects 1/sqrt(head_dim); otherwise finite and > 0. The packed
  * kernels track each row's maximum of the unscaled scores and mask with -inf
  * before scaling, which needs a positive scale; a negative one is rejected
