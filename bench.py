@@ -14,7 +14,11 @@ Printed: one JSON line. `value` is decode tokens/s (B / step time). The
 `roofline` object prices the decode kernel's algorithmic bytes (every visible
 K/V row once, plus q, out and the new k/v) against the 8 TB/s HBM peak.
 `cpu_baseline` times the CPU oracle on the whole last timed step, on the
-host's cores.
+host's cores, and `parity` compares that step's outputs with the oracle's
+(every sequence and head) and every window slot of the cache after the last
+step with the ring rule. `device` records the hardware as the runtime reports
+it; the read, matrix-core and per-CU probes give the ceilings the fractions
+are read against.
 Secondary lines of the same JSON: the full-attention contrast (cache L_m + T)
 at a few decode lengths, and the packed 32K masked forward (both prefix modes)
 and its backward, a multi-document 32K pack, the prefill -> decode hand-off
