@@ -539,7 +539,7 @@ def main():
             "flop_convention": "2.5x the forward: five products of 2 d flop per visible pair (S, dP, dV, dK, "
                                "dQ); the kernels execute seven (S and dP are formed in both the dQ and "
                                "the dK/dV pass)",
-            "calls": "lse-producing forward excluded; pre-pass, dQ, dK/dV and reduction kernels included"}
+            "calls": "lse-producing forward excluded; dQ (with the per-row D and lse terms), dK/dV and reduction kernels included"}
         del ws_b
         result["masked_32k"] = {"workload": mw.name, "seq_len": mw.seq_len, "ref_len": mw.ref_len,
                                 "window": mw.window, "heads": mw.heads, **masked}
@@ -582,7 +582,7 @@ def main():
             "backward": {"ms": ms_vb, "algorithmic_flop": 2.5 * fl_v,
                          "TFLOPs": 2.5 * fl_v / (ms_vb * 1e-3) / 1e12,
                          "frac_of_bf16_peak": 2.5 * fl_v / (ms_vb * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                         "calls": "rswa_masked_attn_bwd_varlen (pre-pass, dQ, dK/dV); flop convention as "
+                         "calls": "rswa_masked_attn_bwd_varlen (dQ, dK/dV); flop convention as "
                                   "for the single-sequence backward"}}
         del Qd, Kd, Vd, Od, cu_d, refs_d, Gd, dq, dk, dv, lse, ws_v
 

@@ -123,8 +123,8 @@ struct MaskedBwdParams {
   void *dq;
   void *dk;
   void *dv;
-  float *nd_row;   // workspace [H][n_pad]: -(dO_i . O_i)
-  float *nls;      // workspace [H][n_pad]: -lse_i / scale (raw score units)
+  float *nd_row;   // workspace [H][n_pad]: -(dO_i . O_i), written by the dQ kernel
+  float *nls;      // workspace [H][n_pad]: -lse_i / scale (raw score units), likewise
   float *part_dk;  // workspace [parts][H][kpre][d]: partial dK of the segment's key blocks
   float *part_dv;  // workspace [parts][H][kpre][d]
   int32_t seq_len, n_pad, ref_len, window, heads, prefix_mode;

@@ -64,16 +64,6 @@ constexpr float kSumHi = 32768.f;  // a lane's block sum above this raises the r
 
 typedef uint16_t Tile[kBN * kD];  // one 64-row K or V block
 
-// The other half-wave's copy of x (lanes l and l ^ 32 exchange).
-__device__ __forceinline__ float swap_halves_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float swap_halves_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 __global__ __launch_bounds__(64 * kWaves, 2) void masked_attn_kernel(MaskedParams p) {
   __shared__ Tile k_sm[2], v_sm[2];
   const int H = p.heads, n = p.window;

@@ -6,12 +6,13 @@
 //   dV_j = sum_i P_ij dO_i,   dP_ij = dO_i . v_j,   D_i = dO_i . O_i,
 //   dS_ij = P_ij (dP_ij - D_i),   dQ_i = scale sum_j dS_ij k_j,
 //   dK_j = scale sum_i dS_ij q_i.
-// P is recomputed from the forward's per-row log-sum-exp. Three kernels:
-//  * bwd_pre_kernel: D_i and the log-sum-exp in base 2 per (head, row);
+// P is recomputed from the forward's per-row log-sum-exp. Two kernels (and a
+// reduction when the long walks are split):
 //  * bwd_dq_kernel: one workgroup per 128 query rows x head, the forward's
-//    block walk; per 32-key tile S^T = K Q^T and dP^T = V dO^T on matrix cores
-//    (K and V row fragments from LDS, Q and dO rows resident), dS^T in
-//    registers, dQ^T += K^T dS^T with K^T from transposing LDS reads;
+//    block walk; it first forms D_i and -lse_i / scale of its rows (stored for
+//    the next kernel), then per 32-key tile S^T = K Q^T and dP^T = V dO^T on
+//    matrix cores (K and V row fragments from LDS, Q and dO rows resident),
+//    dS^T in registers, dQ^T += K^T dS^T with K^T from transposing LDS reads;
 //  * bwd_dkdv_kernel: one workgroup per 128 keys x head walking the 32-row
 //    query blocks that see any of its keys; producer waves (K and V rows of 32
 //    keys resident) form S = Q K^T and dP = dO V^T (Q, dO row fragments from
@@ -35,39 +36,6 @@ namespace rswa {
 namespace {
 
 using namespace tile;
-
-// ---------------------------------------------------------------- pre-pass
-// nd[h][i] = -sum_d dO[i][h][d] O[i][h][d] and nls[h][i] = -lse[h][i] / scale (in
-// the units of the unscaled scores), stored so because the dK/dV products start
-// from them. Rows past N in each head's padded stretch get 0 for both.
-// 4 waves x 4 rows per block; 16 lanes per row, 16 bytes each.
-__global__ __launch_bounds__(256) void bwd_pre_kernel(MaskedBwdParams p) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t row = (int64_t)blockIdx.x * 16 + wave * 4 + (lane >> 4);  // = h * Np + i
-  const int c = lane & 15;
-  const int Np = p.n_pad;
-  if (row >= (int64_t)p.heads * Np) return;
-  const int h = (int)(row / Np), i = (int)(row % Np);
-  float acc = 0.f;
-  if (i < p.seq_len) {
-    const int64_t off = ((int64_t)i * p.heads + h) * kD + c * 8;
-    const u32x4_t g = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(p.dout) + off);
-    const u32x4_t o = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(p.out) + off);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = fmaf(__uint_as_float(g[e] << 16), __uint_as_float(o[e] << 16), acc);
-      acc = fmaf(__uint_as_float(g[e] & 0xffff0000u), __uint_as_float(o[e] & 0xffff0000u), acc);
-    }
-  }
-  acc += __shfl_xor(acc, 1, 64);
-  acc += __shfl_xor(acc, 2, 64);
-  acc += __shfl_xor(acc, 4, 64);
-  acc += __shfl_xor(acc, 8, 64);
-  if (c == 0) {
-    p.nd_row[row] = -acc;
-    p.nls[row] = i < p.seq_len ? -p.lse[(int64_t)h * p.seq_len + i] / p.scale : 0.f;
-  }
-}
 
 // --------------------------------------------------------------- dQ kernel
 constexpr int kBMq = 128;    // query rows per workgroup (4 waves x 32)
@@ -140,10 +108,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(MaskedBwdParams p) {
       gf[ks] = as_bf16x8(q_ok ? *reinterpret_cast<const u32x4_t *>(Gg + r + ks * 16 + hi * 8) : zero);
     }
   }
-  const int64_t rq = (int64_t)h * p.n_pad + row0 + (q_ok ? qi : 0);
-  const float Dq = -p.nd_row[rq];
+  // D_i = dO_i . O_i of this lane's row (the lane holds half of the row's dO,
+  // at the same places as its O loaded here; lane l ^ 32 the other half) and
+  // -lse_i / scale, computed here and stored for the dK/dV pass, whose
+  // products start from them.
+  float dpart = 0.f;
+  if (q_ok) {
+    const uint16_t *Orow = static_cast<const uint16_t *>(p.out) + base + (int64_t)qi * stride;
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) {
+      const u32x4_t o = *reinterpret_cast<const u32x4_t *>(Orow + ks * 16 + hi * 8);
+      const u32x4_t g = __builtin_bit_cast(u32x4_t, gf[ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dpart = fmaf(__uint_as_float(g[e] << 16), __uint_as_float(o[e] << 16), dpart);
+        dpart = fmaf(__uint_as_float(g[e] & 0xffff0000u), __uint_as_float(o[e] & 0xffff0000u), dpart);
+      }
+    }
+  }
+  const float Dq = swap_halves_sum(dpart);
+  const float nls_q = q_ok ? -p.lse[(int64_t)h * p.seq_len + row0 + qi] / p.scale : 0.f;
+  if (q_ok && hi == 0) {
+    const int64_t rq = (int64_t)h * p.n_pad + row0 + qi;
+    p.nd_row[rq] = -Dq;
+    p.nls[rq] = nls_q;
+  }
   const float c = p.scale_log2;
-  const float nlc = p.nls[rq] * c;  // -lse in base 2
+  const float nlc = nls_q * c;  // -lse in base 2
 
   // The keys row qi sees inside each segment form one interval [lo, lo + span):
   // the reference segment up to L_m (or up to the row itself for a causal row
@@ -770,16 +761,12 @@ int64_t masked_bwd_dkdv_grid(int32_t heads, int32_t parts, int32_t nkb_pre, int3
 }
 
 hipError_t launch_masked_bwd(const MaskedBwdParams &p, hipStream_t s) {
-  const int64_t rows = (int64_t)p.heads * p.n_pad;
-  hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const bool pack = p.cu_seqlens != nullptr;
   const int64_t rows_max = pack ? p.max_seq_len : p.seq_len;
   const int64_t samples = pack ? p.num_seqs : 1;
   const int64_t gq = samples * ((rows_max + kBMq - 1) / kBMq) * p.heads;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)gq), dim3(256), 0, s, p);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t gk = pack ? samples * p.heads * ((rows_max + kBK - 1) / kBK)
                           : masked_bwd_dkdv_grid(p.heads, p.parts, p.nkb_pre, p.nkb_win);

@@ -58,6 +58,17 @@ __device__ __forceinline__ uint32_t tr_off(int lane, int db, int h2) {
   return row * kRowBytes + 16 * chunk + 8 * (q & 1);
 }
 
+// x combined with the other half-wave's copy (lanes l and l ^ 32 exchange
+// through v_permlane32_swap): their max, or their sum.
+__device__ __forceinline__ float swap_halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap_halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // The 32x32x16 operand for 16-row step st and d block db from two transposing reads.
 __device__ __forceinline__ bf16x8_t tr_operand(const char *tile, uint32_t off0, uint32_t off1, int st) {
   const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(tile + off0 + 16 * st * kRowBytes));
